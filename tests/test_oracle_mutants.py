@@ -1,0 +1,68 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant is a copy of moon_oracle.cpp with one plausible mistake (a dropped
+term, a wrong index or sign, a swapped order, a wrong rounding).  It is
+compiled to a temporary library and the pin tests run against it in a
+subprocess; every mutant must make them fail.  The oracle source itself is
+never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "histogram_drops_other_ranks": ("T[e] += 1;", "T[e] += (r == 0);"),
+    "stream_offset_off_by_one_group": ("      Pe[e] = acc;\n      acc += T[e];",
+                                       "      acc += T[e];\n      Pe[e] = acc;"),
+    "alias_take_from_original_load": ("int64_t f = C - rem[u];", "int64_t f = C - L[u];"),
+    "alias_last_donor_first": ("int o = large.front();", "int o = large.back();"),
+    "slot_index_ignores_segment_start": ("idx = q - std::max(Pe[e], seg_a[u]);",
+                                         "idx = q - Pe[e];"),
+    "layout_without_padding": ("acc += padded(n[ug], P);", "acc += n[ug];"),
+    "zero_fill_from_group_start": ("zfr[ug * 2 + 0] = (int32_t)(start[ug] + n[ug]);",
+                                   "zfr[ug * 2 + 0] = (int32_t)(start[ug]);"),
+    "dedup_counts_itself": ("for (int k2 = 0; k2 < k; ++k2)", "for (int k2 = 0; k2 <= k; ++k2)"),
+    "dup_loff_begin_wrong": ("rec[1] = (int32_t)nd;", "rec[1] = (int32_t)ng;"),
+    "route_weight_of_first_k": ("if (w != nullptr) wwin[G] = w[t * K + k];",
+                                "if (w != nullptr) wwin[G] = w[t * K];"),
+    "combine_drops_weight": ("double c = weighted ? (double)wk : 1.0;", "double c = 1.0;"),
+    "dst_decode_off_by_one": ("return d >= 0 ? (int64_t)d : -(int64_t)d - 1;",
+                              "return d >= 0 ? (int64_t)d : -(int64_t)d;"),
+    "rounding_truncates": ("double r = std::nearbyint(scaled);", "double r = std::trunc(scaled);"),
+    "remote_stats_counts_all_slots": ("if (etc[(size_t)u * B + j] >= 0) {", "if (true) {"),
+}
+
+PIN_TESTS = ["tests/test_oracle_plan.py", "tests/test_oracle_data.py"]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(os.path.join(ROOT, "oracle", "moon_oracle.cpp")) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    mdir = tmp_path / "oracle"
+    mdir.mkdir()
+    (mdir / "moon_oracle.cpp").write_text(src.replace(old, new))
+    (mdir / "moon_oracle.h").write_text(open(os.path.join(ROOT, "oracle", "moon_oracle.h")).read())
+    so = str(mdir / "liboracle_mutant.so")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", str(mdir / "moon_oracle.cpp"),
+                    "-o", so], check=True)
+    env = dict(os.environ, MOON_ORACLE_SO=so)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PIN_TESTS], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
+
+
+def test_unmutated_oracle_passes_pins():
+    oracle._load()  # builds if needed
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PIN_TESTS], cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
