@@ -1,0 +1,393 @@
+// moon_api.hip — host side of the C ABI declared in include/moon.h.
+//
+// Validation happens here, before anything is launched; kernels only see
+// shapes that fit their grids and LDS tables.  Context = the pages' Buffer
+// ("MoonEP Public API Visual Guide", Buffer(...): validate the topology,
+// derive the capacities, allocate the hidden and metadata windows); plan = the
+// MoonEPCommPlan arrays plus cu_seqlens and a status word.
+#include <new>
+
+#include "moon_internal.h"
+
+namespace {
+
+using moon::Dims;
+
+constexpr uint32_t kCtxMagic = 0x43584E4Du, kPlanMagic = 0x504C4E4Du, kDead = 0u;
+
+int64_t round_up(int64_t n, int64_t p) { return (n + p - 1) / p * p; }
+
+int bits_for(int n) {  // bits of the values 0..n-1
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) {
+      changed = hipSetDevice(dev) == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+moon_status make_dims(const moon_config* c, Dims* d) {
+  if (c == nullptr || c->flags != 0) return MOON_ERR_INVALID_ARG;
+  if (c->R < 1 || c->E < 1 || c->K < 1 || c->S < 1 || c->H < 1 || c->token_padding < 1)
+    return MOON_ERR_INVALID_ARG;
+  if (c->E % c->R != 0) return MOON_ERR_TOPOLOGY;
+  if (c->R > moon::kMaxR || c->E > moon::kMaxE || c->K > moon::kMaxK || c->H % 8 != 0 ||
+      c->H > 65536 || c->H < 8)
+    return MOON_ERR_UNSUPPORTED;
+  const int Eg = c->E / c->R;
+  const int B = c->B <= 0 ? Eg : c->B;
+  if ((int64_t)c->R * B > moon::kMaxSlotsTotal) return MOON_ERR_UNSUPPORTED;
+  const int64_t routes = (int64_t)c->R * c->S * c->K;
+  const int64_t nvs =
+      round_up((int64_t)c->S * c->K + (int64_t)(Eg + B) * (c->token_padding - 1), c->token_padding);
+  if (routes >= (int64_t)1 << 31 || (int64_t)c->R * nvs >= (int64_t)1 << 31)
+    return MOON_ERR_UNSUPPORTED;
+  d->R = c->R;
+  d->E = c->E;
+  d->K = c->K;
+  d->S = c->S;
+  d->H = c->H;
+  d->B = B;
+  d->P = c->token_padding;
+  d->Eg = Eg;
+  d->EB = c->E + B;
+  d->NvS = (int32_t)nvs;
+  // Planner tiles: at most kMaxTiles in all, never across a rank boundary,
+  // at least 64 tokens each when a rank has that many.
+  int tpr = moon::kMaxTiles / c->R;
+  if (tpr < 1) tpr = 1;
+  int tt = (c->S + tpr - 1) / tpr;
+  const int min_tt = c->S < 64 ? c->S : 64;
+  if (tt < min_tt) tt = min_tt;
+  d->tile_tok = tt;
+  d->tiles_per_rank = (c->S + tt - 1) / tt;
+  d->ntiles = c->R * d->tiles_per_rank;
+  d->ebits = bits_for(c->E);
+  d->rbits = bits_for(c->R);
+  return MOON_OK;
+}
+
+bool ctx_ok(const moon_ctx* c) { return c != nullptr && c->magic == kCtxMagic; }
+bool plan_ok(const moon_comm_plan* p) { return p != nullptr && p->magic == kPlanMagic && ctx_ok(p->ctx); }
+
+size_t carve(size_t& off, size_t bytes) {
+  size_t at = (off + 255) & ~(size_t)255;
+  off = at + bytes;
+  return at;
+}
+
+// Offsets of the plan arrays inside one allocation.
+struct PlanOffsets {
+  size_t dst, etc, zfr, rstats, dup_groups, dup_loffs, dup_counts, cu, status, total;
+};
+
+PlanOffsets plan_offsets(const Dims& d) {
+  PlanOffsets o;
+  size_t off = 0;
+  const size_t i4 = sizeof(int32_t);
+  o.dst = carve(off, (size_t)d.R * d.S * d.K * i4);
+  o.etc = carve(off, (size_t)d.R * d.B * i4);
+  o.zfr = carve(off, (size_t)d.R * d.EB * 2 * i4);
+  o.rstats = carve(off, (size_t)d.R * 2 * i4);
+  o.dup_groups = carve(off, (size_t)d.R * d.NvS * 3 * i4);
+  o.dup_loffs = carve(off, (size_t)d.R * d.NvS * i4);
+  o.dup_counts = carve(off, (size_t)d.R * 2 * i4);
+  o.cu = carve(off, (size_t)d.R * d.EB * i4);
+  o.status = carve(off, i4);
+  o.total = (off + 255) & ~(size_t)255;
+  return o;
+}
+
+moon::PlanArrays plan_arrays(void* mem, const PlanOffsets& o) {
+  char* b = static_cast<char*>(mem);
+  moon::PlanArrays a;
+  a.dst = reinterpret_cast<int32_t*>(b + o.dst);
+  a.etc = reinterpret_cast<int32_t*>(b + o.etc);
+  a.zfr = reinterpret_cast<int32_t*>(b + o.zfr);
+  a.rstats = reinterpret_cast<int32_t*>(b + o.rstats);
+  a.dup_groups = reinterpret_cast<int32_t*>(b + o.dup_groups);
+  a.dup_loffs = reinterpret_cast<int32_t*>(b + o.dup_loffs);
+  a.dup_counts = reinterpret_cast<int32_t*>(b + o.dup_counts);
+  a.cu = reinterpret_cast<int32_t*>(b + o.cu);
+  a.status = reinterpret_cast<int32_t*>(b + o.status);
+  return a;
+}
+
+moon_status new_plan(moon_ctx* ctx, moon_comm_plan** out) {
+  const PlanOffsets o = plan_offsets(ctx->d);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, o.total) != hipSuccess) return MOON_ERR_OOM;
+  moon_comm_plan* p = new (std::nothrow) moon_comm_plan;
+  if (p == nullptr) {
+    (void)hipFree(mem);
+    return MOON_ERR_OOM;
+  }
+  p->magic = kPlanMagic;
+  p->ctx = ctx;
+  p->mem = mem;
+  p->bytes = o.total;
+  p->a = plan_arrays(mem, o);
+  *out = p;
+  return MOON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
+  if (out == nullptr) return MOON_ERR_INVALID_ARG;
+  *out = nullptr;
+  Dims d;
+  moon_status st = make_dims(cfg, &d);
+  if (st != MOON_OK) return st;
+
+  moon_ctx* c = new (std::nothrow) moon_ctx;
+  if (c == nullptr) return MOON_ERR_OOM;
+  c->magic = kCtxMagic;
+  c->d = d;
+  c->hidden_win = nullptr;
+  c->w_win = nullptr;
+  c->scratch_mem = nullptr;
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return MOON_ERR_HIP;
+  }
+  const size_t rows = (size_t)d.R * d.NvS;
+  size_t off = 0;
+  const size_t i4 = sizeof(int32_t);
+  const size_t o_cnt = carve(off, (size_t)d.E * d.ntiles * i4);
+  const size_t o_bad = carve(off, (size_t)d.ntiles * i4);
+  const size_t o_base = carve(off, (size_t)d.E * d.ntiles * i4);
+  const size_t o_pe = carve(off, (size_t)d.E * i4);
+  const size_t o_keep = carve(off, (size_t)d.R * i4);
+  const size_t o_donor = carve(off, (size_t)d.R * i4);
+  const size_t o_sa = carve(off, (size_t)d.R * i4);
+  const size_t o_sb = carve(off, (size_t)d.R * i4);
+  const size_t o_slot = carve(off, (size_t)d.E * i4);
+  const size_t o_dup = carve(off, (size_t)d.ntiles * d.R * 2 * i4);
+  if (hipMalloc(&c->hidden_win, rows * d.H * 2) != hipSuccess ||
+      hipMalloc(reinterpret_cast<void**>(&c->w_win), rows * 4) != hipSuccess ||
+      hipMalloc(&c->scratch_mem, off) != hipSuccess) {
+    moon_ctx_destroy(&c);
+    return MOON_ERR_OOM;
+  }
+  if (hipMemset(c->hidden_win, 0, rows * d.H * 2) != hipSuccess ||
+      hipMemset(c->w_win, 0, rows * 4) != hipSuccess ||
+      hipMemset(c->scratch_mem, 0, off) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    moon_ctx_destroy(&c);
+    return MOON_ERR_HIP;
+  }
+  char* b = static_cast<char*>(c->scratch_mem);
+  c->sc.tile_cnt = reinterpret_cast<int32_t*>(b + o_cnt);
+  c->sc.tile_bad = reinterpret_cast<int32_t*>(b + o_bad);
+  c->sc.base = reinterpret_cast<int32_t*>(b + o_base);
+  c->sc.Pe = reinterpret_cast<int32_t*>(b + o_pe);
+  c->sc.keep = reinterpret_cast<int32_t*>(b + o_keep);
+  c->sc.donor = reinterpret_cast<int32_t*>(b + o_donor);
+  c->sc.seg_a = reinterpret_cast<int32_t*>(b + o_sa);
+  c->sc.seg_b = reinterpret_cast<int32_t*>(b + o_sb);
+  c->sc.slot_of = reinterpret_cast<int32_t*>(b + o_slot);
+  c->sc.tile_dup = reinterpret_cast<int32_t*>(b + o_dup);
+  *out = c;
+  return MOON_OK;
+}
+
+moon_status moon_ctx_layout(const moon_ctx* ctx, moon_layout* out) {
+  if (!ctx_ok(ctx) || out == nullptr) return MOON_ERR_INVALID_ARG;
+  out->N = ctx->d.S * ctx->d.K;
+  out->NvS = ctx->d.NvS;
+  out->NvS_padded = ctx->d.NvS;
+  out->E_plus_B = ctx->d.EB;
+  out->B = ctx->d.B;
+  out->hidden_windows = ctx->hidden_win;
+  out->weight_windows = ctx->w_win;
+  return MOON_OK;
+}
+
+void moon_ctx_destroy(moon_ctx** ctx) {
+  if (ctx == nullptr || *ctx == nullptr) return;
+  moon_ctx* c = *ctx;
+  if (c->magic == kCtxMagic) {
+    DeviceGuard g(c->device);
+    (void)hipDeviceSynchronize();
+    if (c->hidden_win) (void)hipFree(c->hidden_win);
+    if (c->w_win) (void)hipFree(c->w_win);
+    if (c->scratch_mem) (void)hipFree(c->scratch_mem);
+    c->magic = kDead;
+    delete c;
+  }
+  *ctx = nullptr;
+}
+
+moon_status moon_plan_create(moon_ctx* ctx, moon_comm_plan** out) {
+  if (out == nullptr) return MOON_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!ctx_ok(ctx)) return MOON_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  moon_comm_plan* p = nullptr;
+  moon_status st = new_plan(ctx, &p);
+  if (st != MOON_OK) return st;
+  const int32_t init = moon::kNotPlanned;
+  if (hipMemcpy(p->a.status, &init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) {
+    moon_plan_destroy(&p);
+    return MOON_ERR_HIP;
+  }
+  *out = p;
+  return MOON_OK;
+}
+
+moon_status moon_plan_clone(const moon_comm_plan* src, moon_comm_plan** out, hipStream_t stream) {
+  if (out == nullptr) return MOON_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!plan_ok(src)) return MOON_ERR_INVALID_ARG;
+  DeviceGuard g(src->ctx->device);
+  moon_comm_plan* p = nullptr;
+  moon_status st = new_plan(src->ctx, &p);
+  if (st != MOON_OK) return st;
+  if (hipMemcpyAsync(p->mem, src->mem, src->bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess) {
+    moon_plan_destroy(&p);
+    return MOON_ERR_HIP;
+  }
+  *out = p;
+  return MOON_OK;
+}
+
+void moon_plan_destroy(moon_comm_plan** plan) {
+  if (plan == nullptr || *plan == nullptr) return;
+  moon_comm_plan* p = *plan;
+  if (p->magic == kPlanMagic) {
+    if (p->mem) (void)hipFree(p->mem);
+    p->magic = kDead;
+    delete p;
+  }
+  *plan = nullptr;
+}
+
+moon_status moon_plan_view(const moon_comm_plan* plan, moon_plan_arrays* out) {
+  if (!plan_ok(plan) || out == nullptr) return MOON_ERR_INVALID_ARG;
+  const Dims& d = plan->ctx->d;
+  out->dst = plan->a.dst;
+  out->experts_to_copy = plan->a.etc;
+  out->zero_fill_ranges = plan->a.zfr;
+  out->remote_stats = plan->a.rstats;
+  out->dup_groups = plan->a.dup_groups;
+  out->dup_loffs = plan->a.dup_loffs;
+  out->dup_counts = plan->a.dup_counts;
+  out->cu_seqlens = plan->a.cu;
+  out->status = plan->a.status;
+  out->N = d.S * d.K;
+  out->R = d.R;
+  out->E = d.E;
+  out->B = d.B;
+  out->NvS = d.NvS;
+  out->K = d.K;
+  return MOON_OK;
+}
+
+moon_status moon_plan_status(const moon_comm_plan* plan, hipStream_t stream) {
+  if (!plan_ok(plan)) return MOON_ERR_INVALID_ARG;
+  DeviceGuard g(plan->ctx->device);
+  int32_t bits = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOON_ERR_HIP;
+  if (hipMemcpy(&bits, plan->a.status, sizeof(bits), hipMemcpyDeviceToHost) != hipSuccess)
+    return MOON_ERR_HIP;
+  if (bits & moon::kBadExpert) return MOON_ERR_BAD_EXPERT;
+  if (bits & moon::kHistogram) return MOON_ERR_HISTOGRAM;
+  if (bits & moon::kSlotBudget) return MOON_ERR_SLOT_BUDGET;
+  if (bits & moon::kInternal) return MOON_ERR_INTERNAL;
+  if (bits & moon::kNotPlanned) return MOON_ERR_NOT_PLANNED;
+  return bits == 0 ? MOON_OK : MOON_ERR_INTERNAL;
+}
+
+moon_status moon_plan(moon_ctx* ctx, const int32_t* topk_rsk, const int32_t* tokens_per_expert_re,
+                      moon_comm_plan* plan, hipStream_t stream) {
+  if (!ctx_ok(ctx) || !plan_ok(plan) || topk_rsk == nullptr) return MOON_ERR_INVALID_ARG;
+  if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
+  if (!aligned(topk_rsk, 4) || !aligned(tokens_per_expert_re, 4)) return MOON_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  if (moon::launch_plan(ctx->d, ctx->sc, plan->a, topk_rsk, tokens_per_expert_re, stream) !=
+      hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
+moon_status moon_dispatch(moon_ctx* ctx, const moon_comm_plan* plan, const void* hidden_rsh,
+                          const float* weights_rsk, void* hidden_out, float* weights_out,
+                          uint32_t flags, hipStream_t stream) {
+  if (!ctx_ok(ctx) || !plan_ok(plan) || hidden_rsh == nullptr) return MOON_ERR_INVALID_ARG;
+  if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
+  if ((flags & ~MOON_DISPATCH_FUSED_DUPS) != 0) return MOON_ERR_INVALID_ARG;
+  void* hout = hidden_out != nullptr ? hidden_out : ctx->hidden_win;
+  float* wout = weights_out != nullptr ? weights_out : ctx->w_win;
+  if (!aligned(hidden_rsh, 16) || !aligned(hout, 16) || !aligned(weights_rsk, 4) ||
+      !aligned(wout, 4))
+    return MOON_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  if (moon::launch_dispatch(ctx->d, plan->a, static_cast<const uint16_t*>(hidden_rsh), weights_rsk,
+                            static_cast<uint16_t*>(hout), wout,
+                            (flags & MOON_DISPATCH_FUSED_DUPS) != 0, stream) != hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
+moon_status moon_combine(moon_ctx* ctx, const moon_comm_plan* plan, const void* y_nvsh,
+                         const float* w_nvs, uint32_t flags, void* out_rsh, float* w_rsk_out,
+                         hipStream_t stream) {
+  if (!ctx_ok(ctx) || !plan_ok(plan) || y_nvsh == nullptr || out_rsh == nullptr)
+    return MOON_ERR_INVALID_ARG;
+  if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
+  if ((flags & ~MOON_COMBINE_WEIGHTED) != 0) return MOON_ERR_INVALID_ARG;
+  const bool weighted = (flags & MOON_COMBINE_WEIGHTED) != 0;
+  if ((weighted || w_rsk_out != nullptr) && w_nvs == nullptr) return MOON_ERR_INVALID_ARG;
+  if (!aligned(y_nvsh, 16) || !aligned(out_rsh, 16) || !aligned(w_nvs, 4) || !aligned(w_rsk_out, 4))
+    return MOON_ERR_INVALID_ARG;
+  DeviceGuard g(ctx->device);
+  if (moon::launch_combine(ctx->d, plan->a, static_cast<const uint16_t*>(y_nvsh), w_nvs, weighted,
+                           static_cast<uint16_t*>(out_rsh), w_rsk_out, stream) != hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
+moon_status moon_prefetch_index(moon_ctx* ctx, const moon_comm_plan* plan, int32_t* src_rb2,
+                                hipStream_t stream) {
+  if (!ctx_ok(ctx) || !plan_ok(plan) || src_rb2 == nullptr || !aligned(src_rb2, 4))
+    return MOON_ERR_INVALID_ARG;
+  if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
+  DeviceGuard g(ctx->device);
+  if (moon::launch_prefetch_index(ctx->d, plan->a, src_rb2, stream) != hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
+const char* moon_status_str(moon_status s) {
+  switch (s) {
+    case MOON_OK: return "ok";
+    case MOON_ERR_INVALID_ARG: return "invalid argument";
+    case MOON_ERR_TOPOLOGY: return "E is not divisible by R";
+    case MOON_ERR_UNSUPPORTED: return "sizes beyond the supported limits";
+    case MOON_ERR_OOM: return "device allocation failed";
+    case MOON_ERR_HIP: return "HIP runtime error";
+    case MOON_ERR_PLAN_MISMATCH: return "plan belongs to another context";
+    case MOON_ERR_BAD_EXPERT: return "expert id out of range";
+    case MOON_ERR_SLOT_BUDGET: return "prefetch slot budget exceeded";
+    case MOON_ERR_HISTOGRAM: return "tokens_per_expert disagrees with the routes";
+    case MOON_ERR_NOT_PLANNED: return "plan not filled yet";
+    case MOON_ERR_INTERNAL: return "internal consistency check failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// moon_internal.h — shared definitions of libmoon's host code and kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moon.h"
+
+namespace moon {
+
+constexpr int kWave = 64;
+constexpr int kMaxR = 32;
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 64;
+constexpr int kMaxTiles = 64;       // one lane per tile in the cross-tile scan
+constexpr int kPlanWaves = 16;      // waves per planner workgroup
+constexpr int kPlanThreads = kPlanWaves * kWave;
+constexpr int kMaxSlotsTotal = 8192;  // R * B
+
+// Device status bits of a plan (reported by moon_plan_status).
+constexpr int32_t kBadExpert = 1, kSlotBudget = 2, kHistogram = 4, kNotPlanned = 8, kInternal = 16;
+
+// Sizes shared by all kernels of one context.
+struct Dims {
+  int32_t R, E, K, S, H, B, P;
+  int32_t Eg, EB;          // E/R, E+B
+  int32_t NvS;             // rows per rank window
+  int32_t tile_tok;        // tokens per planner tile (a tile never spans two ranks)
+  int32_t tiles_per_rank;
+  int32_t ntiles;          // R * tiles_per_rank <= kMaxTiles
+  int32_t ebits;           // bits needed for an expert id
+  int32_t rbits;           // bits needed for a rank id
+};
+
+// Planner scratch owned by a context (one allocation).
+struct Scratch {
+  int32_t* tile_cnt;   // [E][ntiles] routes of expert e in tile t
+  int32_t* tile_bad;   // [ntiles] 1 if the tile holds an id outside [0,E)
+  int32_t* base;       // [E][ntiles] routes of e in earlier tiles (global route order)
+  int32_t* Pe;         // [E] start of expert e in its home rank's stream
+  int32_t* keep;       // [R] routes a rank keeps from its own stream
+  int32_t* donor;      // [R] rank a receiver takes from (-1 if none)
+  int32_t* seg_a;      // [R] receiver's segment [seg_a, seg_b) of its donor's stream
+  int32_t* seg_b;      // [R]
+  int32_t* slot_of;    // [R][Eg] slot of the donor's j-th expert on receiver u (-1)
+  int32_t* tile_dup;   // [ntiles][R][2] duplicate groups / rows per destination rank
+};
+
+// Plan arrays (one allocation).
+struct PlanArrays {
+  int32_t *dst, *etc, *zfr, *rstats, *dup_groups, *dup_loffs, *dup_counts, *cu, *status;
+};
+
+}  // namespace moon
+
+struct moon_ctx {
+  uint32_t magic;
+  int device;
+  moon::Dims d;
+  void* hidden_win;      // bf16 [R*NvS, H]
+  float* w_win;          // fp32 [R*NvS]
+  void* scratch_mem;
+  moon::Scratch sc;
+};
+
+struct moon_comm_plan {
+  uint32_t magic;
+  moon_ctx* ctx;
+  void* mem;
+  size_t bytes;
+  moon::PlanArrays a;
+};
+
+namespace moon {
+
+// Kernel launchers (each returns a hipError_t from the launch).
+hipError_t launch_plan(const Dims& d, const Scratch& sc, const PlanArrays& pa, const int32_t* topk,
+                       const int32_t* tpe, hipStream_t s);
+hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* hidden,
+                           const float* w, uint16_t* win, float* wwin, bool fused, hipStream_t s);
+hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y,
+                          const float* wnvs, bool weighted, uint16_t* out, float* wsk,
+                          hipStream_t s);
+// 16-byte vector of raw bits (eight bf16 values).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t dst_global_row(int32_t v) { return v >= 0 ? v : -(int64_t)v - 1; }
+
+hipError_t launch_prefetch_index(const Dims& d, const PlanArrays& pa, int32_t* out, hipStream_t s);
+
+}  // namespace moon

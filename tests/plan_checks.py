@@ -224,11 +224,12 @@ def check_dups_canonical(pv):
         assert got == exp, f"rank {r}: duplicate groups differ"
 
 
-def check_all(pv, topk, readings=True):
+def check_all(pv, topk, readings=True, dups=True):
     check_layout(pv)
     check_routes(pv, topk)
     check_slots(pv)
-    check_dups(pv)
+    if dups:
+        check_dups(pv)
     if readings:
         check_reading_slot_order(pv)
         check_reading_group_order(pv)

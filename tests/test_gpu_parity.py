@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Plan, cu_seqlens, dispatched rows and weights must match bit for bit; combine
+must stay within |d| <= 1e-2 max|ref| + 1e-3 (and within the derived fp32
+bound of parity.combine_bound); gathered weights and the prefetch index are
+bit-exact.  Everything goes through the C ABI (the package binding).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import parity as pt
+import plan_checks as pc
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_balanced_planning_amd as moon
+    return moon, torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, dflags=0, weighted=True,
+             label=""):
+    """Plan + dispatch + combine on the GPU with full comparisons to the oracle."""
+    import torch
+    say(f"[case] {label} R={R} E={E} K={K} S={S} H={H} B={B} P={P} dflags={dflags}")
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    plan = moon.moon_plan_create(ctx)
+    try:
+        topk_d = pt.to_dev(topk, dev)
+        moon.moon_plan(ctx, topk_d, None, plan)
+        moon.moon_dispatch(ctx, plan, pt.bf16_to_dev(hidden, dev),
+                           pt.to_dev(w, dev) if w is not None else None, flags=dflags)
+        win, wwin = moon.window_tensors(ctx)
+        y_d = pt.bf16_to_dev(y, dev)
+        out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
+        wsk = torch.empty((R, S, K), dtype=torch.float32, device=dev) if w is not None else None
+        moon.moon_combine(ctx, plan, y_d, wwin if w is not None else None,
+                          moon.MOON_COMBINE_WEIGHTED if weighted else 0, out, wsk)
+        pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
+        moon.moon_prefetch_index(ctx, plan, pidx)
+        assert moon.moon_plan_status(plan) == moon.MOON_OK
+        got = pt.gpu_plan_arrays(plan)
+
+        ref = oracle.plan(topk, E, ctx.B, P)
+        assert ref.status == oracle.OK and ref.NvS == ctx.NvS
+        pt.compare_plan(got, ref)
+        pc.check_all(pt.gpu_plan_view(got, ref), topk, dups=R * S <= 4096)
+
+        ewin, ewwin = oracle.dispatch(ref, hidden, w)
+        src = oracle.row_sources(ref)
+        cov = src != -2
+        gwin = pt.dev_bits(win)
+        assert np.array_equal(gwin[cov], ewin[cov]), "dispatched rows differ"
+        if w is not None:
+            assert np.array_equal(wwin.cpu().numpy()[cov].view(np.uint32),
+                                  ewwin[cov].view(np.uint32)), "dispatched weights differ"
+
+        eout, ewsk, acc = oracle.combine(ref, y, ewwin, weighted=weighted)
+        rows = np.arange(R * ref.NvS)
+        absum = pt.abs_sum(ref.dst.reshape(R * S, K), rows, y,
+                           ewwin if ewwin is not None else np.zeros(R * ref.NvS, np.float32),
+                           weighted).reshape(R, S, H)
+        dmax, ndiff = pt.check_combine(pt.dev_bits(out), eout, acc, absum, K)
+        say(f"   combine max|d|={dmax:.3g} bf16 mismatches={ndiff}/{eout.size}")
+        if w is not None:
+            assert np.array_equal(wsk.cpu().numpy().view(np.uint32), ewsk.view(np.uint32))
+        assert np.array_equal(pidx.cpu().numpy(), oracle.prefetch_index(ref))
+        return ref, got
+    finally:
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
+
+
+def workload_inputs(config, level=0):
+    wl = synth.workload(config, level)
+    R, S, H, E, K, B, P = (wl[k] for k in ("R", "S", "H", "E", "K", "B", "P"))
+    nvs = oracle.nvs(R, E, K, S, B, P)
+    hidden = synth.hidden_bf16(wl["seed"], R, S, H)
+    y = synth.y_bf16(wl["seed"], R * nvs, H)
+    return wl, hidden, y
+
+
+@pytest.mark.parametrize("config,level", [(1, 0), (2, 0), (4, 0), (4, 1), (4, 2), (4, 3)])
+def test_workload_full_parity(env, config, level):
+    moon, dev = env
+    wl, hidden, y = workload_inputs(config, level)
+    say(f"[workload] config {config} level {level} maxvio={wl['maxvio']:.3f}")
+    run_full(moon, dev, wl["topk"], wl["w"], hidden, y, wl["R"], wl["E"], wl["K"], wl["S"],
+             wl["H"], wl["B"], wl["P"], label=wl["name"])
+
+
+def _edge_topk(rng, R, S, K, E, mode):
+    if mode == "uniform":
+        return np.stack([rng.permutation(E)[:K] for _ in range(R * S)]).reshape(R, S, K).astype(
+            np.int32)
+    if mode == "skewed":
+        p = 1.0 / np.arange(1, E + 1) ** 2.0
+        p /= p.sum()
+        return np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(R * S)]).reshape(
+            R, S, K).astype(np.int32)
+    if mode == "repeats":  # ids may repeat inside a token; a third of tokens all expert 0
+        t = rng.integers(0, E, size=(R, S, K)).astype(np.int32)
+        t[:, ::3, :] = 0
+        return t
+    if mode == "one_expert":
+        return np.zeros((R, S, K), np.int32) + (E - 1)
+    if mode == "home_block":  # every token picks its K experts inside one rank
+        Eg = E // R
+        h = rng.integers(0, R, size=R * S)
+        return np.stack([h[i] * Eg + rng.choice(Eg, K, replace=Eg < K)
+                         for i in range(R * S)]).reshape(R, S, K).astype(np.int32)
+    raise ValueError(mode)
+
+
+EDGE = [
+    # label, R, E, K, S, H, B, P, mode
+    ("single-rank", 1, 8, 2, 100, 64, 0, 4, "uniform"),
+    ("top1", 4, 16, 1, 130, 32, 0, 8, "skewed"),
+    ("ragged-tiles", 3, 12, 3, 1000, 24, 0, 5, "skewed"),
+    ("one-expert-per-rank", 4, 4, 2, 64, 16, 0, 2, "repeats"),
+    ("no-padding", 4, 16, 4, 77, 16, 0, 1, "skewed"),
+    ("min-width", 2, 8, 2, 33, 8, 0, 4, "uniform"),
+    ("wide-rows", 2, 8, 2, 40, 8192, 0, 16, "uniform"),
+    ("dsv3-rows", 2, 16, 4, 40, 7168, 0, 8, "skewed"),
+    ("repeated-ids", 4, 8, 4, 50, 64, 0, 4, "repeats"),
+    ("all-one-expert", 2, 8, 3, 64, 32, 0, 8, "one_expert"),
+    ("home-block-dedup", 4, 32, 8, 96, 64, 0, 16, "home_block"),
+    ("many-ranks", 32, 64, 3, 40, 16, 0, 4, "skewed"),
+    ("k16", 4, 64, 16, 50, 16, 0, 4, "uniform"),
+    ("k64", 2, 8, 64, 9, 8, 0, 4, "repeats"),
+    ("b-small-ok", 4, 16, 2, 64, 16, 1, 4, "uniform"),
+    ("large-e", 8, 512, 8, 128, 16, 0, 8, "skewed"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_shapes(env, case):
+    moon, dev = env
+    label, R, E, K, S, H, B, P, mode = case
+    rng = np.random.default_rng(zlib.crc32(label.encode()))
+    topk = _edge_topk(rng, R, S, K, E, mode)
+    Bx = B if B > 0 else E // R
+    ref = oracle.plan(topk, E, Bx, P)
+    if ref.status == oracle.SLOT_BUDGET:
+        pytest.skip("this routing needs more slots than B")
+    w = rng.random((R, S, K)).astype(np.float32)
+    hidden = synth.bf16_normal(rng.integers(1 << 62), 0, R * S * H).reshape(R, S, H)
+    y = synth.bf16_normal(rng.integers(1 << 62), 0, R * ref.NvS * H).reshape(R * ref.NvS, H)
+    run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, label=label)
+
+
+def test_fused_duplicates_and_unweighted_round_trip(env):
+    """FUSED_DUPS writes the same windows; unweighted combine of the
+    dispatched windows gives K * x exactly (closed form)."""
+    import torch
+    moon, dev = env
+    wl, hidden, _ = workload_inputs(2)
+    R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+    say(f"[case] fused + round trip {wl['name']}")
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    plan = moon.moon_plan_create(ctx)
+    try:
+        moon.moon_plan(ctx, pt.to_dev(wl["topk"], dev), None, plan)
+        h_d = pt.bf16_to_dev(hidden, dev)
+        moon.moon_dispatch(ctx, plan, h_d, None)
+        win, _ = moon.window_tensors(ctx)
+        a = win.clone()
+        win.zero_()
+        moon.moon_dispatch(ctx, plan, h_d, None, flags=moon.MOON_DISPATCH_FUSED_DUPS)
+        assert torch.equal(a.view(torch.int16), win.view(torch.int16))
+        out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
+        moon.moon_combine(ctx, plan, win, None, 0, out)
+        exp = (K * h_d.float()).to(torch.bfloat16)  # K*x is exact in fp32
+        assert torch.equal(out.view(torch.int16), exp.view(torch.int16))
+    finally:
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
+
+
+def test_clone_repeat_and_backward_reuse(env):
+    """A plan is bit-reproducible, clone() copies it, and dispatching a second
+    tensor with an existing plan (the backward path) needs no new planning."""
+    import torch
+    moon, dev = env
+    wl, hidden, _ = workload_inputs(1)
+    R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    p1, p2 = moon.moon_plan_create(ctx), moon.moon_plan_create(ctx)
+    try:
+        t = pt.to_dev(wl["topk"], dev)
+        moon.moon_plan(ctx, t, None, p1)
+        moon.moon_plan(ctx, t, None, p2)
+        a, b = pt.gpu_plan_arrays(p1), pt.gpu_plan_arrays(p2)
+        for k in a:
+            if k not in ("dup_groups", "dup_loffs"):
+                assert np.array_equal(a[k], b[k])
+        c = moon.moon_plan_clone(p1)
+        torch.cuda.synchronize()
+        cc = pt.gpu_plan_arrays(c)
+        for k in a:
+            assert np.array_equal(a[k], cc[k])
+        # backward: a gradient dispatched with the saved plan
+        g = synth.bf16_normal(77, 0, R * S * H).reshape(R, S, H)
+        out = torch.zeros((R * ctx.NvS, H), dtype=torch.bfloat16, device=dev)
+        moon.moon_dispatch(ctx, c, pt.bf16_to_dev(g, dev), None, hidden_out=out)
+        ref = oracle.plan(wl["topk"], E, B, P)
+        ewin, _ = oracle.dispatch(ref, g, None)
+        cov = oracle.row_sources(ref) != -2
+        assert np.array_equal(pt.dev_bits(out)[cov], ewin[cov])
+        moon.moon_plan_destroy(c)
+    finally:
+        moon.moon_plan_destroy(p1)
+        moon.moon_plan_destroy(p2)
+        moon.moon_ctx_destroy(ctx)
+
+
+@pytest.mark.parametrize("what", ["bad_high", "bad_negative", "histogram", "slot_budget",
+                                  "not_planned", "tpe_ok"])
+def test_device_status_and_skip(env, what):
+    """Data errors set the plan status; later kernels write nothing."""
+    import torch
+    moon, dev = env
+    R, E, K, S, H, P = 2, 8, 2, 8, 16, 2
+    B = 4
+    topk = np.tile(np.array([[0, 1], [2, 3], [4, 5], [6, 7]], np.int32), (R, 2, 1))
+    tpe = None
+    expect = moon.MOON_OK
+    if what == "bad_high":
+        topk[1, 3, 1] = E
+        expect = moon.MOON_ERR_BAD_EXPERT
+    elif what == "bad_negative":
+        topk[0, 0, 0] = -1
+        expect = moon.MOON_ERR_BAD_EXPERT
+    elif what in ("histogram", "tpe_ok"):
+        tpe = np.stack([np.bincount(topk[r].reshape(-1), minlength=E) for r in range(R)]).astype(
+            np.int32)
+        if what == "histogram":
+            tpe[1, 2] += 1
+            expect = moon.MOON_ERR_HISTOGRAM
+    elif what == "slot_budget":
+        topk = np.array([0] * 16 + [1] * 6 + [2] * 5 + [3] * 5, np.int32).reshape(R, S, K)
+        B = 2
+        expect = moon.MOON_ERR_SLOT_BUDGET
+    elif what == "not_planned":
+        expect = moon.MOON_ERR_NOT_PLANNED
+    say(f"[case] status {what}")
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    plan = moon.moon_plan_create(ctx)
+    try:
+        if what != "not_planned":
+            moon.moon_plan(ctx, pt.to_dev(topk, dev),
+                           pt.to_dev(tpe, dev) if tpe is not None else None, plan)
+        win, wwin = moon.window_tensors(ctx)
+        win.fill_(3.0)
+        wwin.fill_(5.0)
+        hidden = torch.ones((R, S, H), dtype=torch.bfloat16, device=dev)
+        moon.moon_dispatch(ctx, plan, hidden, torch.ones((R, S, K), device=dev))
+        out = torch.full((R, S, H), 7.0, dtype=torch.bfloat16, device=dev)
+        moon.moon_combine(ctx, plan, win, wwin, moon.MOON_COMBINE_WEIGHTED, out)
+        st = moon.moon_plan_status(plan)
+        assert st == expect, moon.moon_status_str(st)
+        if expect != moon.MOON_OK:
+            assert bool((win.float() == 3.0).all()) and bool((wwin == 5.0).all())
+            assert bool((out.float() == 7.0).all())
+        assert oracle.plan(topk, E, B, P, tokens_per_expert=tpe).status == \
+            {moon.MOON_OK: 0, moon.MOON_ERR_BAD_EXPERT: -7, moon.MOON_ERR_HISTOGRAM: -9,
+             moon.MOON_ERR_SLOT_BUDGET: -8, moon.MOON_ERR_NOT_PLANNED: 0}[expect]
+    finally:
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
+
+
+def test_plan_mismatch_is_rejected(env):
+    moon, dev = env
+    c1 = moon.moon_ctx_create(2, 8, 2, 8, 16, 4, 2)
+    c2 = moon.moon_ctx_create(2, 8, 2, 8, 16, 4, 2)
+    p = moon.moon_plan_create(c1)
+    try:
+        import torch
+        with pytest.raises(moon.MoonError) as ei:
+            moon.moon_plan(c2, torch.zeros((2, 8, 2), dtype=torch.int32, device=dev), None, p)
+        assert ei.value.status == moon.MOON_ERR_PLAN_MISMATCH
+    finally:
+        moon.moon_plan_destroy(p)
+        moon.moon_ctx_destroy(c1)
+        moon.moon_ctx_destroy(c2)
