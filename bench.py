@@ -1,0 +1,340 @@
+"""Benchmark of the balanced expert-parallel hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+plan (histogram, balance, layout, placement, duplicate records) -> dispatch
+(scatter + zero-fill + dedup epilogue) -> combine (weighted K-sum + weight
+gather) -> prefetch index.  Inputs are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3]
+
+Prints one JSON line.  `value` is the dispatch+combine algorithmic HBM bytes
+of a step divided by the measured time of the whole step (plan included), in
+GB/s; the line also carries tokens/s, per-call times (HIP events on the
+stream the kernels run on), a maxvio sweep on the same shapes, the roofline
+of the dominant kernel and the oracle timed on the host as a CPU baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+METRIC = "dispatch+combine HBM GB/s (% of peak) and tokens/s vs maxvio; plan µs"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Inputs:
+    """One batch of seeded synthetic input, resident on the GPU."""
+
+    def __init__(self, moon, ctx, config, seed, alpha, dev):
+        import torch
+
+        import synth
+        import synth.gpu as sg
+        c = synth.CONFIGS[config]
+        R, E, K, S, H = c["R"], c["E"], c["K"], c["S"], c["H"]
+        topk, w = synth.routing(config, seed, alpha)
+        self.maxvio = synth.maxvio(topk, E)
+        self.topk = torch.from_numpy(topk).to(dev)
+        self.w = torch.from_numpy(w).to(dev)
+        self.hidden = sg.hidden(seed, R, S, H, dev)
+        self.y = sg.y(seed, R * ctx.NvS, H, dev)
+        self.out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
+        self.wsk = torch.empty((R, S, K), dtype=torch.float32, device=dev)
+        self.pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
+        self.plan = moon.moon_plan_create(ctx)
+
+
+def algorithmic_bytes(moon, ctx, plan):
+    """Bytes the method must move in dispatch and combine for this plan."""
+    c = ctx.cfg
+    R, S, K, H = c.R, c.S, c.K, c.H
+    pt = {k: v.cpu().numpy() for k, v in moon.plan_tensors(plan).items()}
+    n_route = R * S * K
+    n_grp = int(pt["dup_counts"][:, 0].sum())
+    n_dup = int(pt["dup_counts"][:, 1].sum())
+    z = pt["zero_fill_ranges"]
+    n_pad = int((z[..., 1] - z[..., 0]).sum())
+    row = 2 * H
+    d_min = (row * R * S + row * n_route + row * n_pad + 4 * n_route * 3 + 4 * n_pad
+             + 12 * n_grp + 4 * n_dup)
+    dispatch = d_min + row * n_dup  # the epilogue re-reads each duplicate's primary
+    combine = row * n_route + row * R * S + 4 * n_route * 2 + 4 * n_route  # + weight gather
+    return dict(dispatch=dispatch, dispatch_minimal=d_min, combine=combine, n_route=n_route,
+                n_dup=n_dup, n_grp=n_grp, n_pad=n_pad,
+                slots_used=int(pt["remote_stats"][:, 0].sum()),
+                routes_in_slots=int(pt["remote_stats"][:, 1].sum()))
+
+
+def run_steps(moon, ctx, sets, steps, warmup, stream):
+    """Warm up, then time exactly `steps` steps; per-call HIP events on `stream`."""
+    import torch
+    win, wwin = moon.window_tensors(ctx)
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        moon.moon_plan(ctx, s.topk, None, s.plan, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        moon.moon_combine(ctx, s.plan, s.y, wwin, moon.MOON_COMBINE_WEIGHTED, s.out, s.wsk,
+                          stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        moon.moon_prefetch_index(ctx, s.plan, s.pidx, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for s in sets:
+        st = moon.moon_plan_status(s.plan, stream)
+        if st != moon.MOON_OK:
+            raise RuntimeError(f"plan status {moon.moon_status_str(st)}")
+
+    # whole-step timing: K steps back to back
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t0.elapsed_time(t1) / steps
+
+    # per-call timing: the same steps again, each call bracketed by events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    calls = {"plan": 0.0, "dispatch": 0.0, "combine": 0.0, "prefetch_index": 0.0}
+    for ev in evs:
+        calls["plan"] += ev[0].elapsed_time(ev[1])
+        calls["dispatch"] += ev[1].elapsed_time(ev[2])
+        calls["combine"] += ev[2].elapsed_time(ev[3])
+        calls["prefetch_index"] += ev[3].elapsed_time(ev[4])
+    calls = {k: v / steps * 1e3 for k, v in calls.items()}  # microseconds
+    return ms_step, wall, calls
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(config, seed, budget_s=12.0):
+    """The oracle, as it stands, on the host: plan + dispatch + combine of the
+    full workload, repeated until about `budget_s` seconds have passed."""
+    import oracle
+    import synth
+    c = synth.CONFIGS[config]
+    R, E, K, S, H, B, P = (c[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+    topk, w = synth.routing(config, seed)
+    hidden = synth.hidden_bf16(seed, R, S, H)
+    nvs = oracle.nvs(R, E, K, S, B, P)
+    y = synth.y_bf16(seed, R * nvs, H)
+    n = 0
+    t_plan = t_disp = t_comb = 0.0
+    t_start = time.perf_counter()
+    bytes_dc = 0
+    while True:
+        t0 = time.perf_counter()
+        pl = oracle.plan(topk, E, B, P)
+        t1 = time.perf_counter()
+        win, wwin = oracle.dispatch(pl, hidden, w)
+        t2 = time.perf_counter()
+        oracle.combine(pl, y, wwin, weighted=True)
+        t3 = time.perf_counter()
+        t_plan += t1 - t0
+        t_disp += t2 - t1
+        t_comb += t3 - t2
+        n += 1
+        if n == 1:
+            n_route = R * S * K
+            n_grp, n_dup = int(pl.dup_counts[:, 0].sum()), int(pl.dup_counts[:, 1].sum())
+            n_pad = int((pl.zero_fill_ranges[..., 1] - pl.zero_fill_ranges[..., 0]).sum())
+            row = 2 * H
+            bytes_dc = (row * R * S + row * n_route + row * n_pad + 4 * n_route * 3 + 4 * n_pad
+                        + 12 * n_grp + 4 * n_dup + row * n_dup) + \
+                       (row * n_route + row * R * S + 4 * n_route * 3)
+        if time.perf_counter() - t_start >= budget_s:
+            break
+    total = t_plan + t_disp + t_comb
+    return {"value": round(bytes_dc * n / total / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"full workload (config {config}, seed {seed}) x {n}: plan "
+                      f"{t_plan / n * 1e3:.1f} ms, dispatch {t_disp / n * 1e3:.1f} ms, combine "
+                      f"{t_comb / n * 1e3:.1f} ms per step on 1 host core; "
+                      f"{R * S * n / total:.0f} tokens/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3])
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run only a plain 1 GiB elementwise copy (scales HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is "
+              "not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate:
+        n = 1 << 30
+        a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.add(a, 0.0, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate": "torch.add(a, 0, out=b)", "bytes_read": n,
+                          "bytes_written": n, "launches": 5}), flush=True)
+        return
+
+    import combine_balanced_planning_amd as moon
+    import synth
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    config = args.workload
+    c = synth.CONFIGS[config]
+    R, E, K, S, H, B, P = (c[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+    log(f"[bench] workload {c['name']}: building inputs")
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    seed = synth.seed_of(config, 0)
+    # two input sets, alternated, so a step never finds the previous step's
+    # data in the 256 MB last-level cache
+    sets = [Inputs(moon, ctx, config, seed, 0.0, dev),
+            Inputs(moon, ctx, config, seed + 500, 0.0, dev)]
+    torch.cuda.synchronize()
+    log("[bench] timing")
+    ms_step, wall, calls = run_steps(moon, ctx, sets, args.steps, args.warmup, stream)
+    nb = algorithmic_bytes(moon, ctx, sets[0].plan)
+    nb1 = algorithmic_bytes(moon, ctx, sets[1].plan)
+    bytes_dc = 0.5 * (nb["dispatch"] + nb["combine"] + nb1["dispatch"] + nb1["combine"])
+    value = bytes_dc / (ms_step * 1e-3) / 1e9
+    t_dc = (calls["dispatch"] + calls["combine"]) * 1e-6
+    dc_gbps = bytes_dc / t_dc / 1e9
+
+    # dominant call and its roofline (combine is a single kernel launch)
+    comb_bytes = 0.5 * (nb["combine"] + nb1["combine"])
+    disp_bytes = 0.5 * (nb["dispatch"] + nb1["dispatch"])
+    if calls["combine"] >= calls["dispatch"]:
+        kname, kbytes, kus = "k_combine", comb_bytes, calls["combine"]
+    else:
+        kname, kbytes, kus = "dispatch (k_dispatch_scatter + k_dispatch_expand)", disp_bytes, \
+            calls["dispatch"]
+    achieved = kbytes / (kus * 1e-6) / 1e9
+    traffic = measured_traffic("k_combine" if kname == "k_combine" else "dispatch",
+                               c["name"])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                "kernel": kname, "algorithmic_bytes_per_launch": int(kbytes),
+                "avg_launch_us": round(kus, 2)}
+
+    sweep = []
+    if not args.no_sweep and config == 2:
+        # maxvio sweep on the same shapes: level "0" is this workload's routing,
+        # then the skewed levels
+        sweep.append({"maxvio": round(sets[0].maxvio, 4), "ms_per_step": round(ms_step, 4),
+                      "GBps": round(value, 1), "tokens_per_s": round(R * S / (ms_step * 1e-3))})
+        for level, target in enumerate(synth.LEVELS[4]):
+            log(f"[bench] maxvio level {target}")
+            s4 = [Inputs(moon, ctx, 4, synth.seed_of(4, level), synth.alpha_for(4, level), dev),
+                  Inputs(moon, ctx, 4, synth.seed_of(4, level) + 500,
+                         synth.alpha_for(4, level), dev)]
+            ms4, _, calls4 = run_steps(moon, ctx, s4, max(10, args.steps // 2), args.warmup,
+                                       stream)
+            b4 = [algorithmic_bytes(moon, ctx, s.plan) for s in s4]
+            by4 = 0.5 * sum(b["dispatch"] + b["combine"] for b in b4)
+            sweep.append({"maxvio": round(s4[0].maxvio, 4), "target": target,
+                          "ms_per_step": round(ms4, 4), "GBps": round(by4 / (ms4 * 1e-3) / 1e9, 1),
+                          "tokens_per_s": round(R * S / (ms4 * 1e-3)),
+                          "plan_us": round(calls4["plan"], 2),
+                          "slots_used": b4[0]["slots_used"],
+                          "routes_in_slots": b4[0]["routes_in_slots"]})
+            for s in s4:
+                moon.moon_plan_destroy(s.plan)
+            del s4
+        times = [p["ms_per_step"] for p in sweep]
+        flat = max(times) / min(times)
+    else:
+        flat = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(config, seed, args.cpu_budget)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded routing, bf16 N(0,1) activations)",
+        "config": {"workload": c["name"], "R": R, "E": E, "K": K, "S": S, "H": H,
+                   "token_padding": P, "B": B, "maxvio": round(sets[0].maxvio, 4),
+                   "global_batch": R * S, "parallelism": "ep emulated as R windows on 1 GPU"},
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "tokens_per_s": round(R * S / (ms_step * 1e-3)),
+        "dispatch_combine_GBps": round(dc_gbps, 1),
+        "tokens_per_s_excl_plan": round(R * S / t_dc),
+        "call_us": {k: round(v, 2) for k, v in calls.items()},
+        "plan_us": round(calls["plan"], 2),
+        "bytes_per_step": {"dispatch": int(disp_bytes), "combine": int(comb_bytes),
+                           "dispatch_minimal": int(0.5 * (nb["dispatch_minimal"] +
+                                                          nb1["dispatch_minimal"])),
+                           "dup_rows": nb["n_dup"], "pad_rows": nb["n_pad"]},
+        "maxvio_sweep": sweep, "sweep_max_over_min_time": round(flat, 4) if flat else None,
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    for s in sets:
+        moon.moon_plan_destroy(s.plan)
+    moon.moon_ctx_destroy(ctx)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
