@@ -337,7 +337,7 @@ int32_t orc_dispatch(int32_t R, int32_t E, int32_t K, int32_t S, int32_t H, int3
   for (int64_t t = 0; t < (int64_t)R * S; ++t) {
     for (int k = 0; k < K; ++k) {
       int64_t G = decode_row(dst[t * K + k]);
-      std::memcpy(win + G * H, hidden + t * H, (size_t)H * 2);
+      if (H > 0) std::memcpy(win + G * H, hidden + t * H, (size_t)H * 2);
       if (w != nullptr) wwin[G] = w[t * K + k];
     }
   }
@@ -346,7 +346,7 @@ int32_t orc_dispatch(int32_t R, int32_t E, int32_t K, int32_t S, int32_t H, int3
       const int32_t* zr = zfr + ((size_t)u * EB + g) * 2;
       for (int64_t row = zr[0]; row < zr[1]; ++row) {
         int64_t G = (int64_t)u * NvS + row;
-        std::memset(win + G * H, 0, (size_t)H * 2);
+        if (H > 0) std::memset(win + G * H, 0, (size_t)H * 2);
         if (w != nullptr) wwin[G] = 0.0f;
       }
     }
