@@ -64,16 +64,30 @@ moon_status make_dims(const moon_config* c, Dims* d) {
   d->Eg = Eg;
   d->EB = c->E + B;
   d->NvS = (int32_t)nvs;
-  // Planner tiles: at most kMaxTiles in all, never across a rank boundary,
-  // at least 64 tokens each when a rank has that many.
-  int tpr = moon::kMaxTiles / c->R;
-  if (tpr < 1) tpr = 1;
-  int tt = (c->S + tpr - 1) / tpr;
-  const int min_tt = c->S < 64 ? c->S : 64;
-  if (tt < min_tt) tt = min_tt;
+  // Planner tiles: about kTileRoutes routes each, never across a rank
+  // boundary, at most one per compute unit and kMaxTiles in all.
+  int max_tiles = moon::kMaxTiles;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0 && cus < max_tiles)
+    max_tiles = cus;
+  int tt = (moon::kTileRoutes + c->K - 1) / c->K;
+  if (tt > c->S) tt = c->S;
+  int tpr = (c->S + tt - 1) / tt;
+  if ((int64_t)c->R * tpr > max_tiles) {
+    tpr = max_tiles / c->R;
+    if (tpr < 1) tpr = 1;
+    tt = (c->S + tpr - 1) / tpr;
+    tpr = (c->S + tt - 1) / tt;
+  }
   d->tile_tok = tt;
-  d->tiles_per_rank = (c->S + tt - 1) / tt;
-  d->ntiles = c->R * d->tiles_per_rank;
+  d->tiles_per_rank = tpr;
+  d->ntiles = c->R * tpr;
+  d->ntiles_pad = (d->ntiles + 3) / 4 * 4;
+  if ((int64_t)tt * c->K >= (int64_t)1 << 24) return MOON_ERR_UNSUPPORTED;  // 24-bit tile counts
+  d->ctok = moon::kWave / c->K;
+  d->tbits = bits_for(d->ctok);
   d->ebits = bits_for(c->E);
   d->rbits = bits_for(c->R);
   return MOON_OK;
@@ -168,8 +182,7 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   const size_t rows = (size_t)d.R * d.NvS;
   size_t off = 0;
   const size_t i4 = sizeof(int32_t);
-  const size_t o_cnt = carve(off, (size_t)d.E * d.ntiles * i4);
-  const size_t o_bad = carve(off, (size_t)d.ntiles * i4);
+  const size_t o_cnt = carve(off, (size_t)(d.E + 1) * d.ntiles_pad * i4);
   const size_t o_base = carve(off, (size_t)d.E * d.ntiles * i4);
   const size_t o_pe = carve(off, (size_t)d.E * i4);
   const size_t o_keep = carve(off, (size_t)d.R * i4);
@@ -177,7 +190,9 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   const size_t o_sa = carve(off, (size_t)d.R * i4);
   const size_t o_sb = carve(off, (size_t)d.R * i4);
   const size_t o_slot = carve(off, (size_t)d.E * i4);
-  const size_t o_dup = carve(off, (size_t)d.ntiles * d.R * 2 * i4);
+  const size_t o_recv = carve(off, (size_t)d.R * 3 * i4);
+  const size_t o_agg = carve(off, (size_t)d.ntiles * d.R * 8);
+  const size_t o_epoch = carve(off, i4);
   if (hipMalloc(&c->hidden_win, rows * d.H * 2) != hipSuccess ||
       hipMalloc(reinterpret_cast<void**>(&c->w_win), rows * 4) != hipSuccess ||
       hipMalloc(&c->scratch_mem, off) != hipSuccess) {
@@ -192,7 +207,6 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   }
   char* b = static_cast<char*>(c->scratch_mem);
   c->sc.tile_cnt = reinterpret_cast<int32_t*>(b + o_cnt);
-  c->sc.tile_bad = reinterpret_cast<int32_t*>(b + o_bad);
   c->sc.base = reinterpret_cast<int32_t*>(b + o_base);
   c->sc.Pe = reinterpret_cast<int32_t*>(b + o_pe);
   c->sc.keep = reinterpret_cast<int32_t*>(b + o_keep);
@@ -200,7 +214,11 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   c->sc.seg_a = reinterpret_cast<int32_t*>(b + o_sa);
   c->sc.seg_b = reinterpret_cast<int32_t*>(b + o_sb);
   c->sc.slot_of = reinterpret_cast<int32_t*>(b + o_slot);
-  c->sc.tile_dup = reinterpret_cast<int32_t*>(b + o_dup);
+  c->sc.recv = reinterpret_cast<int32_t*>(b + o_recv);
+  c->sc.recv_first = c->sc.recv + d.R;
+  c->sc.recv_cnt = c->sc.recv + 2 * d.R;
+  c->sc.tile_agg = reinterpret_cast<uint64_t*>(b + o_agg);
+  c->sc.epoch = reinterpret_cast<uint32_t*>(b + o_epoch);
   *out = c;
   return MOON_OK;
 }

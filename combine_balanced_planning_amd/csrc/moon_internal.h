@@ -12,7 +12,8 @@ constexpr int kWave = 64;
 constexpr int kMaxR = 32;
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 64;
-constexpr int kMaxTiles = 64;       // one lane per tile in the cross-tile scan
+constexpr int kMaxTiles = 256;      // up to four tiles per lane in the cross-tile scan
+constexpr int kTileRoutes = 512;    // routes per planner tile when there are enough tiles
 constexpr int kPlanWaves = 16;      // waves per planner workgroup
 constexpr int kPlanThreads = kPlanWaves * kWave;
 constexpr int kMaxSlotsTotal = 8192;  // R * B
@@ -28,23 +29,36 @@ struct Dims {
   int32_t tile_tok;        // tokens per planner tile (a tile never spans two ranks)
   int32_t tiles_per_rank;
   int32_t ntiles;          // R * tiles_per_rank <= kMaxTiles
+  int32_t ntiles_pad;      // ntiles rounded up to a multiple of 4 (row stride of tile counts)
   int32_t ebits;           // bits needed for an expert id
   int32_t rbits;           // bits needed for a rank id
+  int32_t ctok;            // tokens per chunk (64 / K)
+  int32_t tbits;           // bits needed for a token index inside a chunk
 };
 
 // Planner scratch owned by a context (one allocation).
 struct Scratch {
-  int32_t* tile_cnt;   // [E][ntiles] routes of expert e in tile t
-  int32_t* tile_bad;   // [ntiles] 1 if the tile holds an id outside [0,E)
-  int32_t* base;       // [E][ntiles] routes of e in earlier tiles (global route order)
-  int32_t* Pe;         // [E] start of expert e in its home rank's stream
-  int32_t* keep;       // [R] routes a rank keeps from its own stream
-  int32_t* donor;      // [R] rank a receiver takes from (-1 if none)
-  int32_t* seg_a;      // [R] receiver's segment [seg_a, seg_b) of its donor's stream
-  int32_t* seg_b;      // [R]
-  int32_t* slot_of;    // [R][Eg] slot of the donor's j-th expert on receiver u (-1)
-  int32_t* tile_dup;   // [ntiles][R][2] duplicate groups / rows per destination rank
+  int32_t* tile_cnt;     // [E+1][ntiles_pad] routes of expert e in tile t; row E holds 1
+                         // for a tile with an id outside [0,E); padding columns stay 0
+  int32_t* base;         // [E][ntiles] routes of e in earlier tiles (global route order)
+  int32_t* Pe;           // [E] start of expert e in its home rank's stream
+  int32_t* keep;         // [R] routes a rank keeps from its own stream
+  int32_t* donor;        // [R] rank a receiver takes from (-1 if none)
+  int32_t* seg_a;        // [R] receiver's segment [seg_a, seg_b) of its donor's stream
+  int32_t* seg_b;        // [R]
+  int32_t* slot_of;      // [R][Eg] slot of the donor's j-th expert on receiver u (-1)
+  int32_t* recv;         // [R] receivers in the order they were served (grouped by donor)
+  int32_t* recv_first;   // [R] index in recv of a donor's first receiver
+  int32_t* recv_cnt;     // [R] receivers of a donor
+  uint64_t* tile_agg;    // [ntiles][R] packed (tag, duplicate groups, duplicate rows) per rank
+  uint32_t* epoch;       // [1] tag of the latest planning call
 };
+
+// Words exchanged between workgroups of one launch: a 16-bit call tag and two
+// 24-bit counts, so a reader knows when a word is current without fences.
+__device__ __forceinline__ uint64_t pack_word(uint32_t tag, uint32_t a, uint32_t b) {
+  return ((uint64_t)(tag & 0xFFFFu) << 48) | ((uint64_t)(a & 0xFFFFFFu) << 24) | (b & 0xFFFFFFu);
+}
 
 // Plan arrays (one allocation).
 struct PlanArrays {

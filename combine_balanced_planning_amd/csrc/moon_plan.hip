@@ -1,56 +1,77 @@
 // moon_plan.hip — the online balancing planner for gfx950 (wave64).
 //
-// Four launches on the caller's stream ("MoonEP Public API Visual Guide",
-// Buffer.dispatch: planning turns the S*K routes of every rank into a compact
-// dst map, local offsets, E+B padded groups and duplicate-route metadata):
+// ("MoonEP Public API Visual Guide", Buffer.dispatch: planning turns the S*K
+//  routes of every rank into a compact dst map, local offsets, E+B padded
+//  groups and duplicate-route metadata; MoonEP README: every rank receives
+//  exactly S*K routes, overflow goes to redundant-expert slots taken from at
+//  most one remote home rank.)
 //
-//   k_plan_hist     one workgroup per tile of tokens: per-(expert, tile) route
-//                   counts in LDS, id validation.
-//   k_plan_balance  one workgroup: per-expert scan over tiles (one lane per
-//                   tile), per-home-rank stream offsets, the alias balance
-//                   (every rank gets exactly S*K routes, overflow from at most
-//                   one remote home rank: MoonEP README, "Perfect balance" and
-//                   "How to set B"), slots, padded layout (cu_seqlens,
-//                   zero_fill_ranges), experts_to_copy, remote_stats, status.
-//   k_plan_place    one workgroup per tile: stable within-tile rank of every
-//                   route by a ballot multisplit over the expert id bits and
-//                   per-wave running counters in LDS, then stream position ->
-//                   (destination rank, group, row); primary/duplicate by
-//                   lane shuffles inside each token; signed dst.
-//   k_plan_dups     one workgroup per tile: duplicate records in token order
-//                   (ballot multisplit over destination-rank bits).
+// Three launches on the caller's stream.  Tiles of about 2048 routes (at
+// most one per compute unit) never span two source ranks; a tile is one
+// workgroup of 16 waves; wave w owns a contiguous token range of its tile and
+// walks it in chunks of whole tokens (floor(64/K) tokens), so a token's K
+// routes sit in adjacent lanes.
 //
-// Nothing depends on the order of atomics: LDS atomics only add counts, so
-// the plan is bit-reproducible.  Tiles never span two source ranks, every
-// wave owns a contiguous token range of its tile, and routes are processed in
-// chunks of whole tokens (floor(64/K) tokens per chunk) so a token's K routes
-// sit in adjacent lanes of one wave.
+//   k_plan_count    per tile: per-wave expert counts (LDS atomics) -> per-wave
+//                   prefixes and the tile's totals.
+//   k_plan_balance  one workgroup: per-expert scans over tiles (16-byte rows,
+//                   a lane per four tiles), home stream offsets, the alias
+//                   fill over the R rank loads (one wave, one lane per rank),
+//                   then per rank its slots and padded layout.
+//   k_plan_place    per tile: stable rank of every route = tile base + wave
+//                   prefix + running per-wave counter + rank inside the chunk
+//                   (ballot match over the expert-id bits); stream position
+//                   -> (destination rank, group, row); primary or duplicate by
+//                   a ballot match over (token, destination rank); signed dst.
+//                   Each tile publishes its duplicate counts per rank and
+//                   reads those of the earlier tiles (never of later ones, so
+//                   the wait always ends); then the duplicate records.
+//
+// The few words tiles pass to each other inside k_plan_place are relaxed
+// atomics at agent scope carrying the call's tag in their high half: coherent
+// across the XCDs' L2 caches without fences, and a reader waits for the tag.
+// Bulk data crosses kernel boundaries only.  LDS atomics only add counts, so
+// plans are bit-reproducible.
 #include "moon_internal.h"
 
 namespace moon {
 namespace {
 
+constexpr int kBatch = 16;            // chunks a wave stages in LDS at once
+constexpr int kCuLds = 8192;          // cu_seqlens entries staged in LDS when they fit
+constexpr int kScanBatch = 8;         // experts whose tile counts a wave loads at once
+constexpr int kTilesPerLane = kMaxTiles / kWave;
+constexpr int kMaxSlotsPerRank = kMaxE / 2;  // pieces per receiver <= E/R <= E/2 (R >= 2)
+constexpr uint32_t kSpinLimit = 1u << 24;
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-__device__ __forceinline__ uint64_t lanes_below() {
-  return (lane_id() == 0) ? 0ull : ((~0ull) >> (kWave - lane_id()));
+// Wave index as a scalar, so ranges derived from it stay uniform.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
 
+__device__ __forceinline__ uint64_t below_lane(int l) {
+  return l <= 0 ? 0ull : ((~0ull) >> (kWave - l));
+}
+
+__device__ __forceinline__ uint64_t lanes_below() { return below_lane(lane_id()); }
+
+// Inclusive prefix sum over the 64 lanes with DPP: shifts within rows of 16
+// lanes, then row broadcasts of lanes 15 and 31.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31
   return v;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
+__device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, kWave - 1); }
+
+__device__ __forceinline__ int wave_sum(int v) { return lane63(wave_incl_scan(v)); }
 
 // Lanes of `set` whose `key` equals this lane's key (ballot over key bits).
 __device__ __forceinline__ uint64_t match_key(uint64_t set, int key, int bits) {
@@ -63,10 +84,36 @@ __device__ __forceinline__ uint64_t match_key(uint64_t set, int key, int bits) {
   return peers;
 }
 
-// Order LDS traffic of one wave between consecutive chunks.
+__device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Order the LDS traffic of one wave between consecutive chunks: the LDS
+// executes a wave's operations in issue order, so it is enough to keep the
+// compiler from moving them and to wait for the wave's own LDS operations
+// (not for its global stores).
 __device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_wave_barrier();
+}
+
+// n values from global memory into LDS, eight loads in flight per thread.
+__device__ __forceinline__ void stage_lds(int* __restrict__ dst, const int32_t* __restrict__ src,
+                                          int n) {
+  for (int x0 = 0; x0 < n; x0 += 8 * kPlanThreads) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int x = x0 + j * kPlanThreads + threadIdx.x;
+      v[j] = x < n ? src[x] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int x = x0 + j * kPlanThreads + threadIdx.x;
+      if (x < n) dst[x] = v[j];
+    }
+  }
 }
 
 struct TileRange {
@@ -91,157 +138,178 @@ __device__ __forceinline__ void wave_tokens(const TileRange& tr, int w, int& ws0
 }
 
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kPlanThreads)
-    k_plan_hist(Dims d, const int32_t* __restrict__ topk, int32_t* __restrict__ tile_cnt,
-                int32_t* __restrict__ tile_bad) {
-  __shared__ int hist[kMaxE];
-  const int t = blockIdx.x;
-  const TileRange tr = tile_range(d, t);
-  for (int e = threadIdx.x; e < d.E; e += kPlanThreads) hist[e] = 0;
-  __syncthreads();
-  int bad = 0;
-  const int64_t i0 = ((int64_t)tr.r * d.S + tr.s0) * d.K;
-  const int64_t i1 = ((int64_t)tr.r * d.S + tr.s1) * d.K;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += kPlanThreads) {
-    const int e = topk[i];
-    if ((unsigned)e < (unsigned)d.E) atomicAdd(&hist[e], 1);
-    else bad = 1;
-  }
-  bad = __syncthreads_or(bad);
-  for (int e = threadIdx.x; e < d.E; e += kPlanThreads) tile_cnt[e * d.ntiles + t] = hist[e];
-  if (threadIdx.x == 0) tile_bad[t] = bad;
-}
-
-// ---------------------------------------------------------------------------
-constexpr int kEPerWave = kMaxE / kPlanWaves;
+// Balance, run by the last tile workgroup of k_plan_count.
+struct BalanceLds {
+  int T[kMaxE], Pe[kMaxE];
+  int L[kMaxR], keep[kMaxR], donor[kMaxR], segA[kMaxR], segB[kMaxR];
+  int pref[kPlanWaves][kMaxTiles + 1];       // a wave's tile prefix (histogram check)
+  int nslot[kPlanWaves][kMaxSlotsPerRank];   // a wave's receiver slot sizes
+  int flags;
+};
 
 __global__ void __launch_bounds__(kPlanThreads)
     k_plan_balance(Dims d, const int32_t* __restrict__ tpe, Scratch sc, PlanArrays pa) {
-  __shared__ int sT[kMaxE], sPe[kMaxE];
-  __shared__ int sL[kMaxR], sKeep[kMaxR], sDonor[kMaxR], sSegA[kMaxR], sSegB[kMaxR];
-  __shared__ int sNslot[kMaxSlotsTotal];
-  __shared__ int sAlias[6 * kMaxR];
-  __shared__ int sFlags;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int E = d.E, R = d.R, Eg = d.Eg, B = d.B, EB = d.EB;
+  __shared__ BalanceLds L;
+  const int lane = lane_id(), wave = wave_id();
+  const int E = d.E, R = d.R, Eg = d.Eg, B = d.B, EB = d.EB, nt = d.ntiles, ntp = d.ntiles_pad;
+  if (threadIdx.x == 0) L.flags = 0;
+  __syncthreads();
 
-  if (threadIdx.x == 0) sFlags = 0;
-  __syncthreads();
-  for (int t = threadIdx.x; t < d.ntiles; t += kPlanThreads)
-    if (sc.tile_bad[t]) atomicOr(&sFlags, kBadExpert);
-  __syncthreads();
-  if (sFlags & kBadExpert) {
-    if (threadIdx.x == 0) pa.status[0] = sFlags;
-    return;
+  // Ids outside [0, E) anywhere?  (row E of the tile counts)
+  if (wave == 0) {
+    int4 b = {0, 0, 0, 0};
+    if (lane * 4 < nt) b = *reinterpret_cast<const int4*>(sc.tile_cnt + E * ntp + lane * 4);
+    if (__ballot((b.x | b.y | b.z | b.w) != 0) && lane == 0) atomicOr(&L.flags, kBadExpert);
   }
 
-  // Per-expert exclusive scan over tiles (tiles in global route order).  All
-  // loads of a wave are issued before the first scan.
-  {
-    int vals[kEPerWave];
+  // Phase A: per-expert exclusive scan over tiles (tile order = global route
+  // order; lane l holds tiles 4l..4l+3, one 16-byte load) and expert totals.
+  // Wave w takes experts w, w+16, ..; a batch of eight experts' rows is
+  // loaded first, then their eight scans run back to back.
+  for (int e0 = wave; e0 < E; e0 += kScanBatch * kPlanWaves) {
+    int c[kScanBatch][kTilesPerLane];
 #pragma unroll
-    for (int j = 0; j < kEPerWave; ++j) {
-      const int e = wave + j * kPlanWaves;
-      vals[j] = (e < E && lane < d.ntiles) ? sc.tile_cnt[e * d.ntiles + lane] : 0;
+    for (int j = 0; j < kScanBatch; ++j) {
+      const int e = e0 + j * kPlanWaves;
+      int4 v = {0, 0, 0, 0};
+      if (e < E && lane * 4 < nt) v = *reinterpret_cast<const int4*>(sc.tile_cnt + e * ntp + lane * 4);
+      c[j][0] = v.x;
+      c[j][1] = v.y;
+      c[j][2] = v.z;
+      c[j][3] = v.w;
     }
+    int incl[kScanBatch];
 #pragma unroll
-    for (int j = 0; j < kEPerWave; ++j) {
-      const int e = wave + j * kPlanWaves;
+    for (int j = 0; j < kScanBatch; ++j)
+      incl[j] = wave_incl_scan(c[j][0] + c[j][1] + c[j][2] + c[j][3]);
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      const int e = e0 + j * kPlanWaves;
       if (e >= E) break;
-      const int c = vals[j];
-      const int incl = wave_incl_scan(c);
-      if (lane < d.ntiles) sc.base[e * d.ntiles + lane] = incl - c;
-      const int tot = __shfl(incl, kWave - 1, kWave);
-      if (lane == 0) sT[e] = tot;
+      int run = incl[j] - (c[j][0] + c[j][1] + c[j][2] + c[j][3]);
+#pragma unroll
+      for (int s = 0; s < kTilesPerLane; ++s) {
+        const int t = lane * kTilesPerLane + s;
+        if (t < nt) sc.base[e * nt + t] = run;
+        run += c[j][s];
+      }
+      if (lane == 0) L.T[e] = lane63(incl[j]);
       if (tpe != nullptr) {
-        // routes of e from source rank r = sum over that rank's tiles
-        const int tpr = d.tiles_per_rank;
-        const int before = __shfl(incl, max(lane - tpr, 0), kWave);
-        const int cnt_r = incl - (lane >= tpr ? before : 0);
-        const bool last = lane < d.ntiles && (lane % tpr) == tpr - 1;
-        if (last && tpe[(lane / tpr) * E + e] != cnt_r) atomicOr(&sFlags, kHistogram);
+        // routes of e from each source rank (a rank's tiles are consecutive)
+        int* rc = L.pref[wave];
+        for (int r = lane; r < R; r += kWave) rc[r] = 0;
+        wave_lds_fence();
+#pragma unroll
+        for (int s = 0; s < kTilesPerLane; ++s) {
+          const int t = lane * kTilesPerLane + s;
+          if (t < nt && c[j][s] != 0) atomicAdd(&rc[t / d.tiles_per_rank], c[j][s]);
+        }
+        wave_lds_fence();
+        for (int r = lane; r < R; r += kWave)
+          if (rc[r] != tpe[r * E + e]) atomicOr(&L.flags, kHistogram);
+        wave_lds_fence();
       }
     }
   }
   __syncthreads();
-
   // Stream offsets: home rank h's stream is its experts in ascending id.
   for (int h = wave; h < R; h += kPlanWaves) {
     int carry = 0;
     for (int j0 = 0; j0 < Eg; j0 += kWave) {
       const int j = j0 + lane;
-      const int v = j < Eg ? sT[h * Eg + j] : 0;
+      const int v = j < Eg ? L.T[h * Eg + j] : 0;
       const int incl = wave_incl_scan(v);
       if (j < Eg) {
-        sPe[h * Eg + j] = carry + incl - v;
+        L.Pe[h * Eg + j] = carry + incl - v;
         sc.Pe[h * Eg + j] = carry + incl - v;
       }
-      carry += __shfl(incl, kWave - 1, kWave);
+      carry += lane63(incl);
     }
-    if (lane == 0) sL[h] = carry;
+    if (lane == 0) L.L[h] = carry;
   }
   __syncthreads();
+  if (L.flags & kBadExpert) {
+    if (threadIdx.x == 0) pa.status[0] = L.flags;
+    return;
+  }
 
-  // Balance: alias fill on the R rank loads (R <= 32, one lane; the queues
-  // live in LDS).
-  if (threadIdx.x == 0) {
+  // Phase B, one wave, lane = rank: the alias fill.  Under-loaded ranks, in
+  // ascending order, take what they lack from the lowest over-loaded rank; a
+  // donor pushed below S*K joins the back of the receiver queue.  Donors are
+  // used up in ascending order, so the appended receivers come after all
+  // initial ones and in ascending order too: both queues are bit masks.
+  if (wave == 0) {
     const int C = d.S * d.K;
-    int* rem = sAlias;
-    int* take = sAlias + kMaxR;
-    int* off = sAlias + 2 * kMaxR;
-    int* given = sAlias + 3 * kMaxR;
-    int* small = sAlias + 4 * kMaxR;
-    int* large = sAlias + 5 * kMaxR;
-    int sh = 0, st = 0, lh = 0, lt = 0;
-    for (int h = 0; h < R; ++h) {
-      rem[h] = sL[h];
-      sDonor[h] = -1;
-      take[h] = 0;
-      off[h] = 0;
-      given[h] = 0;
-      if (rem[h] < C) small[st++] = h;
-    }
-    for (int h = 0; h < R; ++h)
-      if (rem[h] > C) large[lt++] = h;
-    while (sh < st) {
-      const int u = small[sh++];
-      if (lh >= lt) {  // cannot happen: the loads sum to R*C
-        sFlags |= kInternal;
+    int rem = lane < R ? L.L[lane] : C;
+    int donor = -1, take = 0, off = 0, given = 0;
+    int recv = 0, rfirst = 0, rcnt = 0;  // lane j: j-th receiver served; lane o: donor o's range
+    uint64_t small = __ballot(rem < C), large = __ballot(rem > C), appended = 0;
+    int served = 0;
+    bool broken = false;
+    while (small | appended) {
+      int u;
+      if (small) {
+        u = __ffsll((unsigned long long)small) - 1;
+        small &= small - 1;
+      } else {
+        u = __ffsll((unsigned long long)appended) - 1;
+        appended &= appended - 1;
+      }
+      if (!large) {  // cannot happen: the loads sum to R*C
+        broken = true;
         break;
       }
-      const int o = large[lh];
-      const int f = C - rem[u];
-      sDonor[u] = o;
-      take[u] = f;
-      off[u] = given[o];
-      given[o] += f;
-      rem[o] -= f;
-      if (rem[o] < C) {
-        ++lh;
-        if (st < kMaxR) small[st++] = o;
-      } else if (rem[o] == C) {
-        ++lh;
+      const int o = __ffsll((unsigned long long)large) - 1;
+      const int f = C - __shfl(rem, u, kWave);
+      const int g_o = __shfl(given, o, kWave);
+      const int rem_o = __shfl(rem, o, kWave) - f;
+      const int cnt_o = __shfl(rcnt, o, kWave);
+      if (lane == u) {
+        donor = o;
+        take = f;
+        off = g_o;
+      }
+      if (lane == o) {
+        given = g_o + f;
+        rem = rem_o;
+        if (cnt_o == 0) rfirst = served;
+        rcnt = cnt_o + 1;
+      }
+      if (lane == served) recv = u;
+      ++served;
+      if (rem_o < C) {
+        large &= large - 1;
+        appended |= 1ull << o;
+      } else if (rem_o == C) {
+        large &= large - 1;
       }
     }
-    for (int h = 0; h < R; ++h) sKeep[h] = rem[h];
-    for (int u = 0; u < R; ++u) {
-      const int o = sDonor[u];
-      sSegA[u] = o >= 0 ? sKeep[o] + off[u] : 0;
-      sSegB[u] = o >= 0 ? sKeep[o] + off[u] + take[u] : 0;
-    }
-    for (int h = 0; h < R; ++h) {
-      sc.keep[h] = sKeep[h];
-      sc.donor[h] = sDonor[h];
-      sc.seg_a[h] = sSegA[h];
-      sc.seg_b[h] = sSegB[h];
+    if (broken && lane == 0) atomicOr(&L.flags, kInternal);
+    const int keep = rem;
+    const int dk = __shfl(keep, donor < 0 ? 0 : donor, kWave);
+    const int sa = donor >= 0 ? dk + off : 0;
+    const int sb = donor >= 0 ? dk + off + take : 0;
+    if (lane < R) {
+      L.keep[lane] = keep;
+      L.donor[lane] = donor;
+      L.segA[lane] = sa;
+      L.segB[lane] = sb;
+      sc.keep[lane] = keep;
+      sc.donor[lane] = donor;
+      sc.seg_a[lane] = sa;
+      sc.seg_b[lane] = sb;
+      sc.recv[lane] = recv;
+      sc.recv_first[lane] = rfirst;
+      sc.recv_cnt[lane] = rcnt;
     }
   }
   __syncthreads();
 
-  // Slots: a receiver's pieces are its donor's experts overlapping its
-  // segment, in ascending expert id, numbered from slot 0.
+  // Phase C, one wave per rank u: its slots as a receiver (the donor's
+  // experts overlapping its segment, ascending id, from slot 0), then the
+  // padded layout of its E+B groups.
   for (int u = wave; u < R; u += kPlanWaves) {
-    const int o = sDonor[u];
+    const int o = L.donor[u];
     int count = 0, routed = 0;
     for (int j0 = 0; j0 < Eg; j0 += kWave) {
       const int j = j0 + lane;
@@ -249,285 +317,419 @@ __global__ void __launch_bounds__(kPlanThreads)
       int len = 0;
       if (o >= 0 && j < Eg) {
         const int e = o * Eg + j;
-        const int lo = max(sPe[e], sSegA[u]);
-        const int hi = min(sPe[e] + sT[e], sSegB[u]);
-        piece = sT[e] > 0 && lo < hi;
+        const int lo = max(L.Pe[e], L.segA[u]);
+        const int hi = min(L.Pe[e] + L.T[e], L.segB[u]);
+        piece = L.T[e] > 0 && lo < hi;
         len = hi - lo;
       }
       const uint64_t m = __ballot(piece);
       const int slot = count + __popcll(m & lanes_below());
-      if (j < Eg) sc.slot_of[u * Eg + j] = (piece && slot < B) ? slot : -1;
-      if (piece) {
-        if (slot < B) {
-          pa.etc[u * B + slot] = o * Eg + j;
-          sNslot[u * B + slot] = len;
-          routed += len;
-        } else {
-          atomicOr(&sFlags, kSlotBudget);
-        }
+      const bool kept = piece && slot < B && slot < kMaxSlotsPerRank;
+      if (j < Eg) sc.slot_of[u * Eg + j] = kept ? slot : -1;
+      if (kept) {
+        pa.etc[u * B + slot] = o * Eg + j;
+        L.nslot[wave][slot] = len;
+        routed += len;
+      } else if (piece) {
+        atomicOr(&L.flags, kSlotBudget);
       }
       count += __popcll(m);
     }
     routed = wave_sum(routed);
-    for (int j = count + lane; j < B; j += kWave) {
-      pa.etc[u * B + j] = -1;
-      sNslot[u * B + j] = 0;
-    }
+    const int used = min(count, B);
+    for (int j = used + lane; j < B; j += kWave) pa.etc[u * B + j] = -1;
     if (lane == 0) {
-      pa.rstats[u * 2 + 0] = min(count, B);
+      pa.rstats[u * 2 + 0] = used;
       pa.rstats[u * 2 + 1] = routed;
     }
-  }
-  __syncthreads();
-
-  // Layout: inclusive padded end offsets of the E+B groups of every rank.
-  if ((sFlags & (kSlotBudget | kHistogram | kInternal)) == 0) {
+    wave_lds_fence();
+    if (count > B) continue;  // slot budget exceeded: no layout for this plan
+    int carry = 0;
     const int P = d.P;
-    for (int u = wave; u < R; u += kPlanWaves) {
-      int carry = 0;
-      for (int g0 = 0; g0 < EB; g0 += kWave) {
-        const int g = g0 + lane;
-        int n = 0;
-        if (g < E) {
-          if (g / Eg == u) n = min(max(sKeep[u] - sPe[g], 0), sT[g]);
-        } else if (g < EB) {
-          n = sNslot[u * B + (g - E)];
-        }
-        const int pad = n == 0 ? 0 : (n + P - 1) / P * P;
-        const int incl = wave_incl_scan(pad);
-        if (g < EB) {
-          const int end = carry + incl;
-          pa.cu[u * EB + g] = end;
-          pa.zfr[(u * EB + g) * 2 + 0] = end - pad + n;
-          pa.zfr[(u * EB + g) * 2 + 1] = end;
-        }
-        carry += __shfl(incl, kWave - 1, kWave);
+    for (int g0 = 0; g0 < EB; g0 += kWave) {
+      const int g = g0 + lane;
+      int n = 0;
+      if (g < E) {
+        if (g / Eg == u) n = min(max(L.keep[u] - L.Pe[g], 0), L.T[g]);
+      } else if (g < EB && g - E < used) {
+        n = L.nslot[wave][g - E];
       }
+      const int pad = n == 0 ? 0 : (n + P - 1) / P * P;
+      const int incl = wave_incl_scan(pad);
+      if (g < EB) {
+        const int end = carry + incl;
+        pa.cu[u * EB + g] = end;
+        pa.zfr[(u * EB + g) * 2 + 0] = end - pad + n;
+        pa.zfr[(u * EB + g) * 2 + 1] = end;
+      }
+      carry += lane63(incl);
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) pa.status[0] = sFlags;
+  if (threadIdx.x == 0) {
+    pa.status[0] = L.flags;
+    const uint32_t next = sc.epoch[0] + 1u;  // tag of this call's words in k_plan_place
+    sc.epoch[0] = next == 0u ? 1u : next;
+  }
 }
 
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kPlanThreads)
-    k_plan_place(Dims d, const int32_t* __restrict__ topk, Scratch sc, PlanArrays pa) {
-  if (pa.status[0] != 0) return;
-  __shared__ int cnt[kPlanWaves * kMaxE];
-  __shared__ int sBase[kMaxE], sPe[kMaxE], sSlot[kMaxE];
-  __shared__ int sKeep[kMaxR], sDonor[kMaxR], sSegA[kMaxR], sSegB[kMaxR];
-  __shared__ int sDup[kMaxR * 2];
-  __shared__ int sFlags;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int E = d.E, R = d.R, K = d.K, Eg = d.Eg, EB = d.EB, NvS = d.NvS;
+    k_plan_count(Dims d, const int32_t* __restrict__ topk, Scratch sc) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int sBad;
+  const int E = d.E;
   const int t = blockIdx.x;
   const TileRange tr = tile_range(d, t);
-
-  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
-    sBase[e] = sc.base[e * d.ntiles + t];
-    sPe[e] = sc.Pe[e];
-    sSlot[e] = sc.slot_of[e];
-  }
-  for (int x = threadIdx.x; x < kPlanWaves * E; x += kPlanThreads) cnt[x] = 0;
-  for (int h = threadIdx.x; h < R; h += kPlanThreads) {
-    sKeep[h] = sc.keep[h];
-    sDonor[h] = sc.donor[h];
-    sSegA[h] = sc.seg_a[h];
-    sSegB[h] = sc.seg_b[h];
-  }
-  for (int x = threadIdx.x; x < R * 2; x += kPlanThreads) sDup[x] = 0;
-  if (threadIdx.x == 0) sFlags = 0;
+  for (int x = threadIdx.x; x < E; x += kPlanThreads) cnt[x] = 0;
+  if (threadIdx.x == 0) sBad = 0;
   __syncthreads();
-
-  int ws0, ws1;
-  wave_tokens(tr, wave, ws0, ws1);
-  const int64_t rowbase = (int64_t)tr.r * d.S;
-  // Pass 1: per-wave expert counts.
-  for (int64_t i = (rowbase + ws0) * K + lane; i < (rowbase + ws1) * K; i += kWave)
-    atomicAdd(&cnt[wave * E + topk[i]], 1);
-  __syncthreads();
-  // Exclusive prefix over waves: routes of e in earlier waves of this tile.
-  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
-    int run = 0;
-    for (int w = 0; w < kPlanWaves; ++w) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = run;
-      run += c;
+  const int64_t i0 = ((int64_t)tr.r * d.S + tr.s0) * d.K, i1 = ((int64_t)tr.r * d.S + tr.s1) * d.K;
+  int bad = 0;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 8 * kPlanThreads) {
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = i + j * kPlanThreads < i1 ? topk[i + j * kPlanThreads] : -2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((unsigned)e[j] < (unsigned)E) atomicAdd(&cnt[e[j]], 1);
+      else if (e[j] != -2) bad = 1;
     }
   }
+  if (bad) atomicOr(&sBad, 1);
   __syncthreads();
-
-  // Pass 2: chunks of whole tokens.
-  const int ctok = kWave / K;
-  const int k = lane % K;
-  for (int tok = ws0; tok < ws1; tok += ctok) {
-    const int nl = min(ctok, ws1 - tok) * K;
-    const bool act = lane < nl;
-    const int64_t i = (rowbase + tok) * K + lane;
-    const int e = act ? topk[i] : 0;
-    const uint64_t peers = match_key(__ballot(act), e, d.ebits);
-    const int rank = __popcll(peers & lanes_below());
-    const int tot = __popcll(peers);
-    int u = 0, G = 0;
-    if (act) {
-      const int pos = sBase[e] + cnt[wave * E + e] + rank;  // position among e's routes
-      const int h = e / Eg;
-      const int q = sPe[e] + pos;                            // position in h's stream
-      int g, idx;
-      if (q < sKeep[h]) {
-        u = h;
-        g = e;
-        idx = q - sPe[e];
-      } else {
-        u = -1;
-        for (int v = 0; v < R; ++v)
-          if (sDonor[v] == h && sSegA[v] <= q && q < sSegB[v]) u = v;
-        const int slot = u >= 0 ? sSlot[u * Eg + (e - h * Eg)] : -1;
-        if (u < 0 || slot < 0) {  // cannot happen for a consistent plan
-          atomicOr(&sFlags, kInternal);
-          u = 0;
-          g = 0;
-          idx = 0;
-        } else {
-          g = E + slot;
-          idx = q - max(sPe[e], sSegA[u]);
-        }
-      }
-      const int start = g == 0 ? 0 : pa.cu[u * EB + g - 1];
-      G = u * NvS + start + idx;
-    }
-    wave_lds_fence();
-    if (act && rank == 0) cnt[wave * E + e] += tot;
-    wave_lds_fence();
-    // Primary = first route of the token to its destination rank.
-    bool dup = false, has_later = false;
-    for (int j = 1; j < K; ++j) {
-      const int ub = __shfl(u, (lane - j) & (kWave - 1), kWave);
-      const int ua = __shfl(u, (lane + j) & (kWave - 1), kWave);
-      if (j <= k && ub == u) dup = true;
-      if (j < K - k && ua == u) has_later = true;
-    }
-    if (act) {
-      pa.dst[i] = dup ? -(G + 1) : G;
-      if (dup) atomicAdd(&sDup[u * 2 + 1], 1);
-      else if (has_later) atomicAdd(&sDup[u * 2 + 0], 1);
-    }
-  }
-  __syncthreads();
-  for (int x = threadIdx.x; x < R * 2; x += kPlanThreads) sc.tile_dup[t * R * 2 + x] = sDup[x];
-  if (threadIdx.x == 0 && sFlags) atomicOr(&pa.status[0], sFlags);
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) sc.tile_cnt[e * d.ntiles_pad + t] = cnt[e];
+  if (threadIdx.x == 0) sc.tile_cnt[E * d.ntiles_pad + t] = sBad;
 }
 
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int dst_row(int v) { return v >= 0 ? v : -v - 1; }
 
-__global__ void __launch_bounds__(kPlanThreads) k_plan_dups(Dims d, Scratch sc, PlanArrays pa) {
-  if (pa.status[0] != 0) return;
-  __shared__ int wc[kPlanWaves * kMaxR * 2];
-  __shared__ int sBaseD[kMaxR * 2];
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int R = d.R, K = d.K, NvS = d.NvS;
+// v of the lane j places below (wave_shr) or above (wave_shl); `fill` where
+// that lane does not exist.
+__device__ __forceinline__ int from_below(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, 0x138, 0xF, 0xF, false);  // wave_shr:1
+}
+__device__ __forceinline__ int from_above(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, 0x130, 0xF, 0xF, false);  // wave_shl:1
+}
+
+// Lanes of `set` whose key equals this lane's (ballot per key bit), with the
+// bit loop unrolled to a compile-time bound.
+template <int kMaxBits>
+__device__ __forceinline__ uint64_t match_bits(uint64_t set, int key, int bits) {
+  uint64_t peers = set;
+#pragma unroll
+  for (int b = 0; b < kMaxBits; ++b) {
+    if (b < bits) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+  }
+  return peers;
+}
+
+struct PlaceLds {
+  int run[kPlanWaves * kMaxE];             // per-wave counts, then running positions
+  int stage[kPlanWaves * kBatch * kWave];  // a wave's staged expert ids, then dst
+  int base[kMaxE], Pe[kMaxE], slot[kMaxE];
+  int keep[kMaxR], segA[kMaxR], segB[kMaxR], recv[kMaxR], rfirst[kMaxR], rcnt[kMaxR];
+  int wc[kPlanWaves * kMaxR * 2];          // per-wave duplicate groups / rows per rank
+  int baseD[kMaxR * 2], tot[kMaxR * 2];
+  int cu[kCuLds];
+  int flags;
+};
+
+template <bool kCuInLds>
+__device__ __forceinline__ int cu_at(const PlaceLds& L, const int32_t* __restrict__ cu, int i) {
+  return kCuInLds ? L.cu[i] : cu[i];
+}
+
+// Duplicate groups and rows of tile-group word w for rank field x.
+__device__ __forceinline__ int word_field(uint64_t w, int f) {
+  return f == 0 ? (int)((w >> 24) & 0xFFFFFFu) : (int)(w & 0xFFFFFFu);
+}
+
+template <bool kCuInLds>
+__device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, const Scratch& sc,
+                           const PlanArrays& pa, PlaceLds& L, uint32_t tag) {
+  const int lane = lane_id(), wave = wave_id();
+  const int E = d.E, R = d.R, K = d.K, Eg = d.Eg, EB = d.EB, NvS = d.NvS, nt = d.ntiles;
   const int t = blockIdx.x;
   const TileRange tr = tile_range(d, t);
-
-  // Duplicate groups / rows of earlier tiles, per destination rank.
-  for (int x = threadIdx.x; x < R * 2; x += kPlanThreads) {
-    int acc = 0;
-    for (int tt = 0; tt < t; ++tt) acc += sc.tile_dup[tt * R * 2 + x];
-    sBaseD[x] = acc;
-    if (t == d.ntiles - 1) pa.dup_counts[x] = acc + sc.tile_dup[t * R * 2 + x];
-  }
-  for (int x = threadIdx.x; x < kPlanWaves * R * 2; x += kPlanThreads) wc[x] = 0;
-  __syncthreads();
-
   int ws0, ws1;
   wave_tokens(tr, wave, ws0, ws1);
   const int64_t rowbase = (int64_t)tr.r * d.S;
-  const int ctok = kWave / K;
+  const int ctok = d.ctok;
+  const int nchunks = (ws1 - ws0 + ctok - 1) / ctok;
   const int k = lane % K;
+  int* st = L.stage + wave * kBatch * kWave;
+  int* run = L.run + wave * E;
+  int* wc = L.wc + wave * R * 2;
+  const bool staged = nchunks <= kBatch;
 
-  // Pass 1: per-wave counts of groups (owners) and duplicates per rank.
-  for (int tok = ws0; tok < ws1; tok += ctok) {
-    const int nl = min(ctok, ws1 - tok) * K;
-    const bool act = lane < nl;
-    const int v = act ? pa.dst[(rowbase + tok) * K + lane] : 0;
-    const int u = dst_row(v) / NvS;
-    const bool dup = act && v < 0;
-    bool owner = false;
-    for (int j = 1; j < K; ++j) {
-      const int ua = __shfl(u, (lane + j) & (kWave - 1), kWave);
-      if (act && !dup && j < K - k && ua == u) owner = true;
+  // ---- Tables and this wave's first batch of routes, all loads in flight together.
+  {
+    int v[kBatch];
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+      const int tok = ws0 + c * ctok;
+      const int nl = (c < nchunks) ? min(ctok, ws1 - tok) * K : 0;
+      v[c] = lane < nl ? topk[(rowbase + tok) * K + lane] : -1;
     }
-    if (owner) atomicAdd(&wc[(wave * R + u) * 2 + 0], 1);
-    if (dup) atomicAdd(&wc[(wave * R + u) * 2 + 1], 1);
+    stage_lds(L.Pe, sc.Pe, E);
+    stage_lds(L.slot, sc.slot_of, E);
+    for (int e = threadIdx.x; e < E; e += kPlanThreads) L.base[e] = sc.base[e * nt + t];
+    if (kCuInLds) stage_lds(L.cu, pa.cu, R * EB);
+    if (threadIdx.x < R) {
+      const int h = threadIdx.x;
+      L.keep[h] = sc.keep[h];
+      L.segA[h] = sc.seg_a[h];
+      L.segB[h] = sc.seg_b[h];
+      L.recv[h] = sc.recv[h];
+      L.rfirst[h] = sc.recv_first[h];
+      L.rcnt[h] = sc.recv_cnt[h];
+    }
+    for (int x = threadIdx.x; x < kPlanWaves * E; x += kPlanThreads) L.run[x] = 0;
+    for (int x = threadIdx.x; x < kPlanWaves * R * 2; x += kPlanThreads) L.wc[x] = 0;
+    if (threadIdx.x == 0) L.flags = 0;
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) st[c * kWave + lane] = v[c];
   }
   __syncthreads();
-  for (int x = threadIdx.x; x < R * 2; x += kPlanThreads) {
-    int run = sBaseD[x];
+  // Per-wave expert counts of the tile (recounted from the routes), then
+  // running positions = tile base + counts of earlier waves.
+  for (int c = 0; c < nchunks; ++c) {
+    const int tok = ws0 + c * ctok;
+    const int nl = min(ctok, ws1 - tok) * K;
+    if (lane < nl) {
+      const int e = staged ? st[c * kWave + lane] : topk[(rowbase + tok) * K + lane];
+      atomicAdd(&run[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) {
+    int acc = L.base[e];
+#pragma unroll
     for (int w = 0; w < kPlanWaves; ++w) {
-      const int c = wc[w * R * 2 + x];
-      wc[w * R * 2 + x] = run;
-      run += c;
+      const int c = L.run[w * E + e];
+      L.run[w * E + e] = acc;
+      acc += c;
     }
   }
   __syncthreads();
 
-  // Pass 2: records.  Within a wave, owners (and duplicates) of one rank are
-  // ranked by lane order, i.e. token order then ascending k.
-  for (int tok = ws0; tok < ws1; tok += ctok) {
+  // ---- Placement.
+  for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
+    if (b0 > 0) {  // later batches (long wave ranges only)
+      int v[kBatch];
+#pragma unroll
+      for (int c = 0; c < kBatch; ++c) {
+        const int tok = ws0 + (b0 + c) * ctok;
+        const int nl = (b0 + c < nchunks) ? min(ctok, ws1 - tok) * K : 0;
+        v[c] = lane < nl ? topk[(rowbase + tok) * K + lane] : -1;
+      }
+#pragma unroll
+      for (int c = 0; c < kBatch; ++c) st[c * kWave + lane] = v[c];
+    }
+    const int cend = min(kBatch, nchunks - b0);
+    for (int c = 0; c < cend; ++c) {
+      const int tok = ws0 + (b0 + c) * ctok;
+      const int e = st[c * kWave + lane];
+      const bool act = e >= 0;
+      const uint64_t peers = match_bits<10>(__ballot(act), act ? e : 0, d.ebits);
+      const int rank = __popcll(peers & lanes_below());
+      int u = -1, G = 0;
+      if (act) {
+        const int pos = run[e] + rank;  // position among e's routes
+        const int h = e / Eg;
+        const int q = L.Pe[e] + pos;    // position in h's stream
+        int g, idx;
+        if (q < L.keep[h]) {
+          u = h;
+          g = e;
+          idx = q - L.Pe[e];
+        } else {
+          const int f0 = L.rfirst[h], nr = L.rcnt[h];
+          for (int j = 0; j < nr; ++j) {
+            const int v = L.recv[f0 + j];
+            if (q < L.segB[v]) {
+              u = v;
+              break;
+            }
+          }
+          const int slot = u >= 0 ? L.slot[u * Eg + (e - h * Eg)] : -1;
+          if (u < 0 || slot < 0) {  // cannot happen for a consistent plan
+            atomicOr(&L.flags, kInternal);
+            u = 0;
+            g = 0;
+            idx = 0;
+          } else {
+            g = E + slot;
+            idx = q - max(L.Pe[e], L.segA[u]);
+          }
+        }
+        const int start = g == 0 ? 0 : cu_at<kCuInLds>(L, pa.cu, u * EB + g - 1);
+        G = u * NvS + start + idx;
+      }
+      wave_lds_fence();
+      if (act && rank == 0) run[e] += __popcll(peers);
+      // Primary = first route of its token to its destination rank; lanes
+      // j places away hold routes of the same token when j <= k (below) or
+      // j < K - k (above).
+      bool dup = false, later = false;
+      int sb = u, sa = u;
+      for (int j = 1; j < K; ++j) {
+        sb = from_below(sb, -1);
+        sa = from_above(sa, -1);
+        if (j <= k && sb == u) dup = true;
+        if (j < K - k && sa == u) later = true;
+      }
+      dup = dup && act;
+      const bool owner = act && !dup && later;
+      const int v = dup ? -(G + 1) : G;
+      if (act) pa.dst[(rowbase + tok) * K + lane] = v;
+      st[c * kWave + lane] = act ? v : INT32_MIN;
+      const int uk = act ? u : 0;
+      const uint64_t gpeers = match_bits<5>(__ballot(owner), uk, d.rbits);
+      const uint64_t dpeers = match_bits<5>(__ballot(dup), uk, d.rbits);
+      if (owner && (gpeers & lanes_below()) == 0) wc[uk * 2 + 0] += __popcll(gpeers);
+      if (dup && (dpeers & lanes_below()) == 0) wc[uk * 2 + 1] += __popcll(dpeers);
+      wave_lds_fence();
+    }
+  }
+  __syncthreads();
+
+  // ---- Per-rank duplicate counts: wave prefixes and the tile's totals.
+  for (int x = threadIdx.x; x < R * 2; x += kPlanThreads) {
+    int acc = 0;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int c = L.wc[w * R * 2 + x];
+      L.wc[w * R * 2 + x] = acc;
+      acc += c;
+    }
+    L.tot[x] = acc;
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < R; u += kPlanThreads)
+    __hip_atomic_store(sc.tile_agg + t * R + u, pack_word(tag, L.tot[u * 2], L.tot[u * 2 + 1]),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // ---- Counts of earlier tiles: for each rank, lane l reads tiles l,
+  // l+64, .. below this one (one packed word each, all in flight together).
+  // Every wait is on a lower tile, which publishes before it waits.
+  bool timeout = false;
+  const uint32_t tag16 = tag & 0xFFFFu;
+  for (int u = wave; u < R; u += kPlanWaves) {
+    uint64_t w[kTilesPerLane];
+#pragma unroll
+    for (int j = 0; j < kTilesPerLane; ++j) {
+      const int tp = j * kWave + lane;
+      w[j] = tp < t ? get_word(sc.tile_agg + tp * R + u) : pack_word(tag, 0, 0);
+    }
+    int sg = 0, sd = 0;
+#pragma unroll
+    for (int j = 0; j < kTilesPerLane; ++j) {
+      const int tp = j * kWave + lane;
+      uint32_t spins = 0;
+      while ((uint32_t)(w[j] >> 48) != tag16) {
+        if (++spins > kSpinLimit) {
+          timeout = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w[j] = get_word(sc.tile_agg + tp * R + u);
+      }
+      sg += word_field(w[j], 0);
+      sd += word_field(w[j], 1);
+    }
+    sg = wave_sum(sg);
+    sd = wave_sum(sd);
+    if (lane == 0) {
+      L.baseD[u * 2 + 0] = sg;
+      L.baseD[u * 2 + 1] = sd;
+    }
+  }
+  if (timeout) atomicOr(&L.flags, kInternal);
+  __syncthreads();
+  if (L.flags != 0) {
+    if (threadIdx.x == 0) atomicOr(&pa.status[0], L.flags);
+    return;
+  }
+  for (int x = threadIdx.x; x < kPlanWaves * R * 2; x += kPlanThreads)
+    L.wc[x] += L.baseD[x % (R * 2)];
+  if (t == nt - 1)
+    for (int x = threadIdx.x; x < R * 2; x += kPlanThreads)
+      pa.dup_counts[x] = L.baseD[x] + L.tot[x];
+  __syncthreads();
+
+  // ---- Duplicate records.  Owners (first route of a token to a rank that
+  // has later routes there) and duplicates of one rank are ranked by lane
+  // order, i.e. token order then ascending k.
+  for (int c = 0; c < nchunks; ++c) {
+    const int tok = ws0 + c * ctok;
     const int nl = min(ctok, ws1 - tok) * K;
     const bool act = lane < nl;
-    const int v = act ? pa.dst[(rowbase + tok) * K + lane] : 0;
+    int v = 0;
+    if (act) v = staged ? st[c * kWave + lane] : pa.dst[(rowbase + tok) * K + lane];
     const int G = dst_row(v);
-    const int u = G / NvS;
-    const int row = G - u * NvS;
+    const int u = act ? G / NvS : -1;
+    const int uk = act ? u : 0;
+    const int row = G - uk * NvS;
     const bool dup = act && v < 0;
-    bool owner = false;
+    const uint64_t dpeers = match_bits<5>(__ballot(dup), uk, d.rbits);
+    const int didx = dup ? wc[uk * 2 + 1] + __popcll(dpeers & lanes_below()) : -1;
+    // later routes of the same token to the same rank: count and first index
+    bool owner_cand = act && !dup;
+    int m = 0, first = -1, sa = u, da = didx;
     for (int j = 1; j < K; ++j) {
-      const int ua = __shfl(u, (lane + j) & (kWave - 1), kWave);
-      if (act && !dup && j < K - k && ua == u) owner = true;
-    }
-    const uint64_t dpeers = match_key(__ballot(dup), u, d.rbits);
-    const uint64_t gpeers = match_key(__ballot(owner), u, d.rbits);
-    const int drank = __popcll(dpeers & lanes_below());
-    const int grank = __popcll(gpeers & lanes_below());
-    int didx = -1;
-    if (dup) {
-      didx = wc[(wave * R + u) * 2 + 1] + drank;
-      pa.dup_loffs[(int64_t)u * NvS + didx] = row;
-    }
-    int first = -1, m = 0;
-    for (int j = 1; j < K; ++j) {
-      const int ua = __shfl(u, (lane + j) & (kWave - 1), kWave);
-      const int da = __shfl(didx, (lane + j) & (kWave - 1), kWave);
-      if (owner && j < K - k && ua == u) {
+      sa = from_above(sa, -1);
+      da = from_above(da, -1);
+      if (j < K - k && sa == u && owner_cand) {
         if (first < 0) first = da;
         ++m;
       }
     }
+    const bool owner = owner_cand && m > 0;
+    const uint64_t gpeers = match_bits<5>(__ballot(owner), uk, d.rbits);
+    if (dup) pa.dup_loffs[(int64_t)uk * NvS + didx] = row;
     if (owner) {
-      const int gidx = wc[(wave * R + u) * 2 + 0] + grank;
-      int32_t* rec = pa.dup_groups + ((int64_t)u * NvS + gidx) * 3;
+      const int gidx = wc[uk * 2 + 0] + __popcll(gpeers & lanes_below());
+      int32_t* rec = pa.dup_groups + ((int64_t)uk * NvS + gidx) * 3;
       rec[0] = row;
       rec[1] = first;
       rec[2] = m;
     }
     wave_lds_fence();
-    if (dup && drank == 0) wc[(wave * R + u) * 2 + 1] += __popcll(dpeers);
-    if (owner && grank == 0) wc[(wave * R + u) * 2 + 0] += __popcll(gpeers);
+    if (dup && (dpeers & lanes_below()) == 0) wc[uk * 2 + 1] += __popcll(dpeers);
+    if (owner && (gpeers & lanes_below()) == 0) wc[uk * 2 + 0] += __popcll(gpeers);
     wave_lds_fence();
   }
+}
+
+__global__ void __launch_bounds__(kPlanThreads)
+    k_plan_place(Dims d, const int32_t* __restrict__ topk, Scratch sc, PlanArrays pa) {
+  __shared__ PlaceLds L;
+  const uint32_t tag = sc.epoch[0];
+  if (pa.status[0] != 0) {
+    // Nothing to place; still publish, so that no later tile waits on this one.
+    for (int u = threadIdx.x; u < d.R; u += kPlanThreads)
+      __hip_atomic_store(sc.tile_agg + blockIdx.x * d.R + u, pack_word(tag, 0, 0),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (d.R * d.EB <= kCuLds) place_tile<true>(d, topk, sc, pa, L, tag);
+  else place_tile<false>(d, topk, sc, pa, L, tag);
 }
 
 }  // namespace
 
 hipError_t launch_plan(const Dims& d, const Scratch& sc, const PlanArrays& pa, const int32_t* topk,
                        const int32_t* tpe, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan_hist, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, topk, sc.tile_cnt,
-                     sc.tile_bad);
+  hipLaunchKernelGGL(k_plan_count, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, topk, sc);
   hipLaunchKernelGGL(k_plan_balance, dim3(1), dim3(kPlanThreads), 0, s, d, tpe, sc, pa);
   hipLaunchKernelGGL(k_plan_place, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, topk, sc, pa);
-  hipLaunchKernelGGL(k_plan_dups, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, sc, pa);
   return hipGetLastError();
 }
 
