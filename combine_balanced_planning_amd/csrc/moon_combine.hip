@@ -1,17 +1,18 @@
-// moon_combine.hip — gather-reduce combine and route-weight gather.
+// moon_combine.hip — gather-reduce combine, route-weight gather, prefetch index.
 //
 // ("MoonEP Public API Visual Guide", Buffer.combine: follow plan.dst, read
 //  the valid rows and perform the top-k reduction for every original token;
 //  route weights are gathered back through the same positive/negative
 //  destination encoding.)
 //
-// One wave per token.  Lanes 0..K-1 decode the token's K dst entries (both
-// signs: every route owns its row) and fetch the K route weights; the loop
-// over k reads one routed row per step with 16-byte loads (eight bf16 per
-// vector), widens to fp32 and accumulates c_k * y in ascending k with a
-// separate multiply and add (the library is built with -ffp-contract=off),
-// then rounds once to bf16 (nearest, ties to even).  Bound: HBM bandwidth
-// (K row reads + one row write per token).
+// A work item is one wave on a slice of 64 vectors (512 bf16) of one token's
+// row.  Lanes 0..K-1 decode the token's K dst entries (both signs: every
+// route owns its row) and fetch the K route weights; the loop over k reads
+// two routed slices at a time with 16-byte loads, widens bf16 to fp32 and
+// accumulates c_k * y in ascending k with a separate multiply and add (the
+// library is built with -ffp-contract=off), then rounds once to bf16
+// (nearest, ties to even).  Bound: HBM bandwidth (K row reads + one row
+// write per token).
 #include "moon_internal.h"
 
 namespace moon {
@@ -19,6 +20,7 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
+constexpr int kUnroll = 2;  // routed slices in flight per wave
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -30,72 +32,54 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int CH>
 __global__ void __launch_bounds__(kThreads)
     k_combine(Dims d, PlanArrays pa, const u32x4* __restrict__ y, const float* __restrict__ wnvs,
               int weighted, u32x4* __restrict__ out, float* __restrict__ wsk) {
   if (pa.status[0] != 0) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (t >= (int64_t)d.R * d.S) return;
   const int V = d.H / 8;
+  const int nsl = (V + kWave - 1) / kWave;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (item >= (int64_t)d.R * d.S * nsl) return;
+  const int64_t t = item / nsl;
+  const int sl = (int)(item - t * nsl);
+  const int j = sl * kWave + lane;  // this lane's vector of the row
   int gl = 0;
   float wl = 0.0f;
   if (lane < d.K) {
     gl = (int)dst_global_row(pa.dst[t * d.K + lane]);
     if (wnvs != nullptr) wl = wnvs[gl];
-    if (wsk != nullptr) wsk[t * d.K + lane] = wl;
+    if (wsk != nullptr && sl == 0) wsk[t * d.K + lane] = wl;
   }
-  for (int c0 = 0; c0 < V; c0 += kWave * CH) {
-    float acc[CH][8];
+  float acc[8];
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int k0 = 0; k0 < d.K; k0 += kUnroll) {
+    u32x4 buf[kUnroll];
+    float ck[kUnroll];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
-    for (int k = 0; k < d.K; ++k) {
+    for (int uu = 0; uu < kUnroll; ++uu) {
+      const int k = min(k0 + uu, d.K - 1);
       const int G = __builtin_amdgcn_readlane(gl, k);
-      const float ck =
-          weighted ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)) : 1.0f;
-      const u32x4* yp = y + (int64_t)G * V;
-      u32x4 buf[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int j = c0 + c * kWave + lane;
-        if (j < V) buf[c] = __builtin_nontemporal_load(yp + j);
-      }
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[c][2 * q + 0] = acc[c][2 * q + 0] + ck * bf16_lo(buf[c][q]);
-          acc[c][2 * q + 1] = acc[c][2 * q + 1] + ck * bf16_hi(buf[c][q]);
-        }
-      }
+      ck[uu] = weighted ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)) : 1.0f;
+      if (j < V && k0 + uu < d.K) buf[uu] = __builtin_nontemporal_load(y + (int64_t)G * V + j);
     }
-    u32x4* op = out + t * V;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int j = c0 + c * kWave + lane;
-      if (j < V) {
-        u32x4 v;
+    for (int uu = 0; uu < kUnroll; ++uu) {
+      if (k0 + uu >= d.K) break;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[q] = bf16_rne(acc[c][2 * q]) | (bf16_rne(acc[c][2 * q + 1]) << 16);
-        __builtin_nontemporal_store(v, op + j);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q + 0] = acc[2 * q + 0] + ck[uu] * bf16_lo(buf[uu][q]);
+        acc[2 * q + 1] = acc[2 * q + 1] + ck[uu] * bf16_hi(buf[uu][q]);
       }
     }
   }
-}
-
-template <int CH>
-hipError_t launch_ch(const Dims& d, const PlanArrays& pa, const uint16_t* y, const float* wnvs,
-                     bool weighted, uint16_t* out, float* wsk, hipStream_t s) {
-  const int64_t tokens = (int64_t)d.R * d.S;
-  const int blocks = (int)((tokens + kWavesPerBlock - 1) / kWavesPerBlock);
-  hipLaunchKernelGGL(k_combine<CH>, dim3(blocks), dim3(kThreads), 0, s, d, pa,
-                     reinterpret_cast<const u32x4*>(y), wnvs, weighted ? 1 : 0,
-                     reinterpret_cast<u32x4*>(out), wsk);
-  return hipGetLastError();
+  if (j < V) {
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
+    __builtin_nontemporal_store(v, out + t * V + j);
+  }
 }
 
 __global__ void k_prefetch_index(Dims d, PlanArrays pa, int32_t* __restrict__ out) {
@@ -112,13 +96,14 @@ __global__ void k_prefetch_index(Dims d, PlanArrays pa, int32_t* __restrict__ ou
 hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y,
                           const float* wnvs, bool weighted, uint16_t* out, float* wsk,
                           hipStream_t s) {
-  const int per_lane = (d.H / 8 + kWave - 1) / kWave;
-  if (per_lane <= 1) return launch_ch<1>(d, pa, y, wnvs, weighted, out, wsk, s);
-  if (per_lane <= 2) return launch_ch<2>(d, pa, y, wnvs, weighted, out, wsk, s);
-  if (per_lane <= 4) return launch_ch<4>(d, pa, y, wnvs, weighted, out, wsk, s);
-  if (per_lane <= 8) return launch_ch<8>(d, pa, y, wnvs, weighted, out, wsk, s);
-  if (per_lane <= 14) return launch_ch<14>(d, pa, y, wnvs, weighted, out, wsk, s);
-  return launch_ch<16>(d, pa, y, wnvs, weighted, out, wsk, s);
+  const int nsl = (d.H / 8 + kWave - 1) / kWave;
+  const int64_t items = (int64_t)d.R * d.S * nsl;
+  const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)blocks), dim3(kThreads), 0, s, d, pa,
+                     reinterpret_cast<const u32x4*>(y), wnvs, weighted ? 1 : 0,
+                     reinterpret_cast<u32x4*>(out), wsk);
+  return hipGetLastError();
 }
 
 // Prefetch index (Guide, Buffer.prefetch_weight: split a slot's expert id
