@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -143,17 +144,124 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
+# Sources whose change invalidates recorded counter readings: the kernels,
+# their launch configuration and the input generator.
+PMC_SOURCES = ["combine_balanced_planning_amd/csrc/moon_internal.h",
+               "combine_balanced_planning_amd/csrc/moon_api.hip",
+               "combine_balanced_planning_amd/csrc/moon_plan.hip",
+               "combine_balanced_planning_amd/csrc/moon_dispatch.hip",
+               "combine_balanced_planning_amd/csrc/moon_combine.hip",
+               "synth/__init__.py"]
+
+
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (else None)."""
-    path = os.path.join(PROFILES, f"pmc_{kernel}_{workload}.json")
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of `workload`, if it was taken on the current sources (else None)."""
+    path = os.path.join(PROFILES, f"pmc_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_hash") != source_hash(rec.get("sources", [])):
         return None
-    return rec.get("bytes_per_launch")
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
+def short_kernel_name(name):
+    """Kernel name without 'void', this library's namespaces and the argument list."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("moon::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    return n.split("(", 1)[0].strip()
+
+
+def read_counter_csv(d):
+    """{kernel: [values per dispatch]} from a rocprofv3 --pmc csv output folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    out = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                out.setdefault(short_kernel_name(row["Kernel_Name"]), []).append(
+                    float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(workload, dirs, commands):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same counters
+    read for a plain 1 GiB copy, and write profiles/pmc_<workload>.{json,md}."""
+    fetch, write, cfetch, cwrite = (read_counter_csv(d) for d in dirs)
+
+    def calib(tab):
+        # the copy kernel is the one launched exactly five times
+        cands = [v for v in tab.values() if len(v) == 5]
+        if len(cands) != 1:
+            raise SystemExit("calibration run: expected one kernel with 5 launches")
+        return (1 << 30) / (sum(cands[0]) / 5 * 1024.0)
+
+    ff, wf = calib(cfetch), calib(cwrite)
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        if not name.startswith("k_"):
+            continue
+        f_kib = sum(fetch[name]) / len(fetch[name])
+        w_kib = sum(write[name]) / len(write[name])
+        kernels[name] = {"launches": len(fetch[name]), "fetch_kib": round(f_kib, 1),
+                         "write_kib": round(w_kib, 1),
+                         "hbm_bytes_per_launch": int(f_kib * 1024 * ff + w_kib * 1024 * wf)}
+    rec = {"workload": workload, "commands": commands,
+           "calibration": {"kernel": "torch.add(a, 0, out=b), 1 GiB read + 1 GiB written",
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "sources": PMC_SOURCES, "source_hash": source_hash(PMC_SOURCES), "kernels": kernels}
+    with open(os.path.join(PROFILES, f"pmc_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    lines = [f"# HBM traffic counters — workload {workload}", "",
+             "Commands (repo root, one MI355X):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", f"Calibration: a plain 1 GiB copy reads {1 / ff:.4f} GiB by FETCH_SIZE and "
+              f"writes {1 / wf:.4f} GiB by WRITE_SIZE; factors {ff:.4f} and {wf:.4f} scale "
+              "the kernels' readings below.", "",
+              "| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM MB per launch |",
+              "|---|---|---|---|---|"]
+    for n, k in kernels.items():
+        lines.append(f"| {n} | {k['launches']} | {k['fetch_kib']:.1f} | {k['write_kib']:.1f} | "
+                     f"{k['hbm_bytes_per_launch'] / 1e6:.2f} |")
+    with open(os.path.join(PROFILES, f"pmc_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(rec))
+
+
+def summarize_trace(workload, d, command, bench_line=None):
+    """Write profiles/kernels_<workload>.md from a rocprofv3 --stats csv folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    lines = [f"# Kernel trace — workload {workload}", "", "Command (repo root, one MI355X):", "",
+             "    " + command, "",
+             "| kernel | calls | total µs | avg µs | min µs | max µs | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    with open(files[0], newline="") as f:
+        for row in csv.DictReader(f):
+            lines.append(f"| {short_kernel_name(row['Name'])} | {row['Calls']} | "
+                         f"{float(row['TotalDurationNs']) / 1e3:.1f} | "
+                         f"{float(row['AverageNs']) / 1e3:.2f} | {float(row['MinNs']) / 1e3:.2f} | "
+                         f"{float(row['MaxNs']) / 1e3:.2f} | {float(row['Percentage']):.1f} |")
+    if bench_line:
+        with open(bench_line) as f:
+            js = [ln for ln in f if ln.startswith("{")]
+        if js:
+            b = json.loads(js[-1])
+            lines += ["", f"Bench line of the same run: step {b['ms_per_step']} ms; HIP-event call "
+                      f"times (µs) {b['call_us']}; roofline {b['roofline']}."]
+    with open(os.path.join(PROFILES, f"kernels_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def cpu_baseline(config, seed, budget_s=12.0):
@@ -213,7 +321,24 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="run only a plain 1 GiB elementwise copy (scales HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR",
+                    help="rocprofv3 csv folders: FETCH_SIZE run, WRITE_SIZE run, and the same two "
+                         "for --calibrate; writes profiles/pmc_<workload>.{json,md}")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="rocprofv3 --kernel-trace --stats csv folder; writes "
+                         "profiles/kernels_<workload>.md")
+    ap.add_argument("--commands", nargs="*", default=[],
+                    help="the profiler commands, recorded in the summary")
+    ap.add_argument("--bench-log", help="log of the traced run (its JSON line is quoted)")
     args = ap.parse_args()
+    if args.summarize_pmc or args.summarize_trace:
+        import synth
+        name = synth.CONFIGS[args.workload]["name"]
+        if args.summarize_pmc:
+            summarize_pmc(name, args.summarize_pmc, args.commands)
+        else:
+            summarize_trace(name, args.summarize_trace, " ".join(args.commands), args.bench_log)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is "
               "not part of this build", file=sys.stderr)
@@ -257,21 +382,24 @@ def main():
     t_dc = (calls["dispatch"] + calls["combine"]) * 1e-6
     dc_gbps = bytes_dc / t_dc / 1e9
 
-    # dominant call and its roofline (combine is a single kernel launch)
+    # Roofline of the dominant kernel: k_combine, the largest single launch of
+    # the step (one launch per combine call, so the call's HIP-event time is
+    # its launch duration).  Dispatch is two launches (scatter + epilogue);
+    # its call-level figure is reported beside it.
     comb_bytes = 0.5 * (nb["combine"] + nb1["combine"])
     disp_bytes = 0.5 * (nb["dispatch"] + nb1["dispatch"])
-    if calls["combine"] >= calls["dispatch"]:
-        kname, kbytes, kus = "k_combine", comb_bytes, calls["combine"]
-    else:
-        kname, kbytes, kus = "dispatch (k_dispatch_scatter + k_dispatch_expand)", disp_bytes, \
-            calls["dispatch"]
-    achieved = kbytes / (kus * 1e-6) / 1e9
-    traffic = measured_traffic("k_combine" if kname == "k_combine" else "dispatch",
-                               c["name"])
+    achieved = comb_bytes / (calls["combine"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": kname, "algorithmic_bytes_per_launch": int(kbytes),
-                "avg_launch_us": round(kus, 2)}
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": measured_traffic("k_combine", c["name"]),
+                "kernel": "k_combine", "algorithmic_bytes_per_launch": int(comb_bytes),
+                "avg_launch_us": round(calls["combine"], 2)}
+    disp_gbps = disp_bytes / (calls["dispatch"] * 1e-6) / 1e9
+    dispatch_roofline = {"kernels": "k_dispatch_scatter + k_dispatch_expand",
+                         "achieved": round(disp_gbps, 1), "unit": "GB/s",
+                         "frac": round(disp_gbps / PEAK_HBM_GBPS, 4),
+                         "algorithmic_bytes_per_call": int(disp_bytes),
+                         "avg_call_us": round(calls["dispatch"], 2)}
 
     sweep = []
     if not args.no_sweep and config == 2:
@@ -328,6 +456,7 @@ def main():
         "maxvio_sweep": sweep, "sweep_max_over_min_time": round(flat, 4) if flat else None,
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
+        "dispatch_roofline": dispatch_roofline,
         "cpu_baseline": cpu,
     }
     for s in sets:
