@@ -2,8 +2,8 @@
 //
 // Validation happens here, before anything is launched; kernels only see
 // shapes that fit their grids and LDS tables.  Context = the pages' Buffer
-// ("MoonEP Public API Visual Guide", Buffer(...): validate the topology,
-// derive the capacities, allocate the hidden and metadata windows); plan = the
+// ("MoonEP Public API Visual Guide", Buffer(...): the constructor checks the
+// topology, fixes the capacities and owns the persistent windows); plan = the
 // MoonEPCommPlan arrays plus cu_seqlens and a status word.
 #include <new>
 

@@ -1,9 +1,9 @@
 // moon_combine.hip — gather-reduce combine, route-weight gather, prefetch index.
 //
-// ("MoonEP Public API Visual Guide", Buffer.combine: follow plan.dst, read
-//  the valid rows and perform the top-k reduction for every original token;
-//  route weights are gathered back through the same positive/negative
-//  destination encoding.)
+// ("MoonEP Public API Visual Guide", Buffer.combine: the reverse of dispatch;
+//  each token's K routed rows, located through plan.dst, are summed back into
+//  token order, and the route weights are read back through the same signed
+//  entries.)
 //
 // A work item is one wave on a slice of 64 vectors (512 bf16) of one token's
 // row.  Lanes 0..K-1 decode the token's K dst entries (both signs: every
@@ -106,8 +106,8 @@ hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y
   return hipGetLastError();
 }
 
-// Prefetch index (Guide, Buffer.prefetch_weight: split a slot's expert id
-// into its owning rank and rank-local row; -1 slots are skipped).
+// Prefetch index (Guide, Buffer.prefetch_weight: a slot's global expert id
+// names its home rank and its row on that rank; a -1 slot is unused).
 hipError_t launch_prefetch_index(const Dims& d, const PlanArrays& pa, int32_t* out, hipStream_t s) {
   const int n = d.R * d.B;
   if (n == 0) return hipSuccess;

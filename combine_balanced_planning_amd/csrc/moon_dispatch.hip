@@ -1,9 +1,9 @@
 // moon_dispatch.hip — dispatch scatter, padding zero-fill and dedup epilogue.
 //
-// ("MoonEP Public API Visual Guide", Buffer.dispatch: decode route
-//  i = s*K + k, copy the primary hidden row to the destination rank, scatter
-//  every routing weight, zero-fill padding, expand locally deduplicated routes
-//  in an epilogue.)
+// ("MoonEP Public API Visual Guide", Buffer.dispatch: route i = s*K + k of a
+//  token; its row goes once to each destination rank, every route weight to
+//  its own row, padding rows become zero, and a second pass on the receiving
+//  rank fills the duplicate routes from their primary row.)
 //
 // The rank windows are one HBM array, so the remote store of the pages is a
 // scatter of 16-byte vectors.  Bound: HBM bandwidth.

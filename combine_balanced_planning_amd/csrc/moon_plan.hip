@@ -1,13 +1,14 @@
 // moon_plan.hip — the online balancing planner for gfx950 (wave64).
 //
-// ("MoonEP Public API Visual Guide", Buffer.dispatch: planning turns the S*K
-//  routes of every rank into a compact dst map, local offsets, E+B padded
-//  groups and duplicate-route metadata; MoonEP README: every rank receives
-//  exactly S*K routes, overflow goes to redundant-expert slots taken from at
-//  most one remote home rank.)
+// ("MoonEP Public API Visual Guide", Buffer.dispatch: the planner maps each
+//  of a rank's S*K routes to a destination row, lays out E+B padded groups
+//  and records which routes are duplicates; MoonEP README, Perfect balance
+//  and How to set B: each rank ends with S*K routes, the excess going to
+//  redundant-expert slots whose experts all come from one remote home rank.)
 //
-// Three launches on the caller's stream.  Tiles of about 2048 routes (at
-// most one per compute unit) never span two source ranks; a tile is one
+// Three launches on the caller's stream.  Tiles of about 512 routes (more
+// when that would give more tiles than compute units) never span two source
+// ranks; a tile is one
 // workgroup of 16 waves; wave w owns a contiguous token range of its tile and
 // walks it in chunks of whole tokens (floor(64/K) tokens), so a token's K
 // routes sit in adjacent lanes.

@@ -29,8 +29,8 @@ const int32_t ST_OK = 0, ST_INVALID = -1, ST_BAD_EXPERT = -7, ST_SLOT_BUDGET = -
 int64_t round_up(int64_t n, int64_t p) { return (n + p - 1) / p * p; }
 
 // Padded size of a group: non-empty groups are padded to a multiple of the
-// token padding; empty groups stay empty (Visual Guide, Buffer(...):
-// "alignment, in rows, for each non-empty physical VM group").
+// token padding; empty groups stay empty (Visual Guide, Buffer(...): the
+// token padding is the row alignment of groups that hold a route).
 int64_t padded(int64_t n, int64_t p) { return n == 0 ? 0 : round_up(n, p); }
 
 float bf16_to_float(uint16_t b) {
@@ -45,8 +45,8 @@ int64_t decode_row(int32_t d) { return d >= 0 ? (int64_t)d : -(int64_t)d - 1; }
 
 // One token: sum its K routed rows in ascending k, optionally scaled by the
 // route weight stored at the route's own row (Visual Guide, Buffer.combine:
-// top-k reduction per original token; weights gathered through the same
-// positive/negative encoding).
+// each token's K contributions are reduced back into its row; the weights
+// are read back through the signed dst entries, both signs alike).
 template <class RowFn, class WFn>
 void combine_token(int32_t K, int32_t H, const int32_t* d, RowFn row, WFn wat, int32_t weighted,
                    uint16_t* out, float* wsk, double* acc) {
@@ -69,8 +69,8 @@ void combine_token(int32_t K, int32_t H, const int32_t* d, RowFn row, WFn wat, i
 
 extern "C" {
 
-// Capacity.  The pages call NvS "S x K real slots plus per-VM-group padding"
-// (README, Integration notation) without a formula.  A rank holds at most Eg
+// Capacity.  The pages define NvS as room for the S*K routes plus the
+// padding of every group (README, Integration notation), without a formula.  A rank holds at most Eg
 // home groups and at most B slot groups, and padding adds fewer than P rows to
 // each non-empty group, so S*K + (Eg+B)*(P-1) rounded up to P always suffices.
 int32_t orc_nvs(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B, int32_t P) {
@@ -82,10 +82,10 @@ int32_t orc_nvs(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B, int32_t P
 }
 
 // Balance (reading): every rank must end with exactly C routes (README,
-// "Perfect balance"), and a rank may take overflow from at most one remote
-// home rank (README, "How to set B": at most one remote home group per rank).
+// Perfect balance), and a rank may take overflow from at most one remote
+// home rank, so at most E/R slot experts (README, How to set B).
 // Under-loaded ranks are served in ascending rank order from the lowest
-// over-loaded rank; a rank keeps its own routes first ("home-first"); a donor
+// over-loaded rank; a rank keeps its own routes first (home-first); a donor
 // pushed below C becomes a receiver itself and joins the back of the queue.
 // This is the Walker/Vose alias-table construction applied to integer loads.
 // `served` receives the receivers in the order they were served.
@@ -234,8 +234,8 @@ int32_t orc_plan(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B, int32_t 
   }
 
   // ---- Layout: cu holds inclusive padded end offsets of the E+B groups
-  // (Visual Guide, dispatch table: "Padded end offset of each physical VM
-  // group"); zero_fill_ranges is the padding tail [start+n, end) of each.
+  // (Visual Guide, dispatch tensor table: cu_seqlens holds the padded end of
+  // every group); zero_fill_ranges is the padding tail [start+n, end) of each.
   std::vector<int64_t> start((size_t)R * EB, 0);
   for (int u = 0; u < R; ++u) {
     int64_t acc = 0;
@@ -274,10 +274,10 @@ int32_t orc_plan(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B, int32_t 
 
   // ---- Dedup and dst.  Within a token, the first route (lowest k) to each
   // destination rank is the primary and carries the row copy; later routes of
-  // the same token to the same rank are local duplicates (Visual Guide:
-  // dispatch "copies the primary hidden row to the destination rank ... and
-  // expands locally deduplicated routes in an epilogue"; combine's
-  // "positive/negative destination encoding").
+  // the same token to the same rank are local duplicates (Visual Guide,
+  // Buffer.dispatch: one row copy per destination rank, duplicates filled on
+  // the receiving rank afterwards; Buffer.combine: the sign of a dst entry
+  // tells the two kinds apart).
   for (int64_t t = 0; t < (int64_t)R * S; ++t) {
     for (int k = 0; k < K; ++k) {
       int64_t i = t * K + k;

@@ -9,10 +9,10 @@
  * inputs.
  *
  * What it computes follows the "MoonEP Public API Visual Guide"
- * (sections "Buffer.dispatch", "Buffer.combine", "Buffer.prefetch_weight",
- * "MoonEPCommPlan") and the MoonEP README (Performance: maxvio equation;
- * Integration: "How to set B").  Where the pages state only guarantees
- * (perfect balance, at most one remote home group per rank) the oracle takes
+ * (sections Buffer.dispatch, Buffer.combine, Buffer.prefetch_weight,
+ * MoonEPCommPlan) and the MoonEP README (Performance: maxvio equation;
+ * Integration: How to set B).  Where the pages state only guarantees
+ * (perfect balance, slot experts from one remote home rank) the oracle takes
  * one deterministic reading, written out in the .cpp next to each step.
  *
  * Conventions (all arrays C-contiguous, caller-owned host memory):
