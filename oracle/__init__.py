@@ -61,6 +61,11 @@ def _bind(lib):
     lib.orc_combine.restype = i32
     lib.orc_combine_rows.argtypes = [i32, i32, i32, vp, i64, vp, vp, vp, i32, vp, vp, vp]
     lib.orc_combine_rows.restype = i32
+    lib.orc_combine_prologue.argtypes = [i32] * 5 + [vp, vp, vp, i32, vp, vp, vp, vp]
+    lib.orc_combine_prologue.restype = i32
+    lib.orc_combine_prologue_rows.argtypes = [i32, i32, i32, i32, vp, i64, vp, vp, vp, i32, vp,
+                                              vp, vp, vp]
+    lib.orc_combine_prologue_rows.restype = i32
     lib.orc_prefetch_index.argtypes = [i32, i32, i32, vp, vp]
     lib.orc_prefetch_index.restype = i32
     lib.orc_bf16_from_double.argtypes = [ctypes.c_double]
@@ -203,6 +208,48 @@ def combine_rows(dst_tok, rows, yrows, wrows=None, weighted=True, lib=None):
     if st != OK:
         raise RuntimeError(f"orc_combine_rows status {st}")
     return out, wsk, acc
+
+
+def combine_prologue(pl, y, wnvs=None, weighted=True, lib=None):
+    """Combine with the duplicate prologue.  Returns (out [R,S,H] uint16,
+    wsk [R,S,K] fp32 or None, acc fp64, folded [R*NvS,H] uint16 = y with
+    every folded primary row replaced)."""
+    lib = lib or _load()
+    y = _c(y, np.uint16)
+    H = y.shape[1]
+    wnvs = _c(wnvs, np.float32)
+    R, S, K = pl.R, pl.S, pl.K
+    out = np.zeros((R, S, H), np.uint16)
+    wsk = np.zeros((R, S, K), np.float32) if wnvs is not None else None
+    acc = np.zeros((R, S, H), np.float64)
+    folded = np.zeros_like(y)
+    st = lib.orc_combine_prologue(R, K, S, H, pl.NvS, _p(pl.dst), _p(y), _p(wnvs),
+                                  int(bool(weighted)), _p(out), _p(wsk), _p(acc), _p(folded))
+    if st != OK:
+        raise RuntimeError(f"orc_combine_prologue status {st}")
+    return out, wsk, acc, folded
+
+
+def combine_prologue_rows(dst_tok, rows, yrows, NvS, wrows=None, weighted=True, lib=None):
+    """combine_prologue for sampled tokens (as combine_rows); returns
+    (out, wsk, acc, folded_rows [M,H])."""
+    lib = lib or _load()
+    dst_tok = _c(dst_tok, np.int32)
+    rows = _c(rows, np.int64)
+    yrows = _c(yrows, np.uint16)
+    wrows = _c(wrows, np.float32)
+    n, K = dst_tok.shape
+    H = yrows.shape[1]
+    out = np.zeros((n, H), np.uint16)
+    wsk = np.zeros((n, K), np.float32) if wrows is not None else None
+    acc = np.zeros((n, H), np.float64)
+    folded = np.zeros_like(yrows)
+    st = lib.orc_combine_prologue_rows(n, K, H, NvS, _p(dst_tok), rows.shape[0], _p(rows),
+                                       _p(yrows), _p(wrows), int(bool(weighted)), _p(out),
+                                       _p(wsk), _p(acc), _p(folded))
+    if st != OK:
+        raise RuntimeError(f"orc_combine_prologue_rows status {st}")
+    return out, wsk, acc, folded
 
 
 def prefetch_index(pl):

@@ -65,6 +65,57 @@ void combine_token(int32_t K, int32_t H, const int32_t* d, RowFn row, WFn wat, i
   }
 }
 
+
+// Combine with a duplicate prologue (Visual Guide, Buffer.combine: before the
+// gather, the rows of a token's duplicate routes on one destination rank are
+// summed into that rank's primary row in fp32; the gather then reads primary
+// rows only).  Per token and destination rank with m >= 2 routes, the folded
+// row is bf16(sum over those routes, ascending k, of c_k * y) with the fp32
+// arithmetic the pages fix (separate multiply and add); it stands for all m
+// routes with coefficient 1.  The outer sum over primaries, ascending k, is
+// float64 and rounded once, as in the plain combine.  `fold(G, bits)`
+// receives every folded primary row.
+template <class RowFn, class WFn, class FoldFn>
+void combine_token_prologue(int32_t K, int32_t H, int64_t NvS, const int32_t* d, RowFn row, WFn wat,
+                            int32_t weighted, uint16_t* out, float* wsk, double* acc, FoldFn fold) {
+  std::vector<double> sum(H, 0.0);
+  std::vector<float> part(H);
+  std::vector<uint16_t> bits(H);
+  for (int k = 0; k < K; ++k) {
+    int64_t G = decode_row(d[k]);
+    if (wsk != nullptr) wsk[k] = wat(G);
+    if (d[k] < 0) continue;  // a duplicate: folded into its primary below
+    std::vector<int> members{k};
+    for (int k2 = k + 1; k2 < K; ++k2)
+      if (d[k2] < 0 && decode_row(d[k2]) / NvS == G / NvS) members.push_back(k2);
+    if (members.size() == 1) {
+      double c = weighted ? (double)wat(G) : 1.0;
+      const uint16_t* y = row(G);
+      for (int h = 0; h < H; ++h) sum[h] += c * (double)bf16_to_float(y[h]);
+      continue;
+    }
+    std::fill(part.begin(), part.end(), 0.0f);
+    for (int m : members) {
+      int64_t Gm = decode_row(d[m]);
+      float c = weighted ? wat(Gm) : 1.0f;
+      const uint16_t* y = row(Gm);
+      for (int h = 0; h < H; ++h) {
+        float prod = c * bf16_to_float(y[h]);
+        part[h] = part[h] + prod;
+      }
+    }
+    for (int h = 0; h < H; ++h) {
+      bits[h] = orc_bf16_from_double((double)part[h]);
+      sum[h] += (double)bf16_to_float(bits[h]);
+    }
+    fold(G, bits.data());
+  }
+  for (int h = 0; h < H; ++h) {
+    out[h] = orc_bf16_from_double(sum[h]);
+    if (acc != nullptr) acc[h] = sum[h];
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -418,6 +469,50 @@ int32_t orc_combine_rows(int32_t n, int32_t K, int32_t H, const int32_t* dst_tok
         [&](int64_t G) { return wrows != nullptr ? wrows[find(G)] : 0.0f; }, weighted,
         out + t * H, wsk_out != nullptr ? wsk_out + t * K : nullptr,
         acc != nullptr ? acc + t * H : nullptr);
+  }
+  return ST_OK;
+}
+
+int32_t orc_combine_prologue(int32_t R, int32_t K, int32_t S, int32_t H, int32_t NvS,
+                             const int32_t* dst, const uint16_t* y, const float* wnvs,
+                             int32_t weighted, uint16_t* out, float* wsk_out, double* acc,
+                             uint16_t* folded) {
+  if (weighted && wnvs == nullptr) return ST_INVALID;
+  if (folded != nullptr) std::memcpy(folded, y, (size_t)R * NvS * H * 2);
+  for (int64_t t = 0; t < (int64_t)R * S; ++t) {
+    combine_token_prologue(
+        K, H, NvS, dst + t * K, [&](int64_t G) { return y + G * H; },
+        [&](int64_t G) { return wnvs != nullptr ? wnvs[G] : 0.0f; }, weighted, out + t * H,
+        wsk_out != nullptr ? wsk_out + t * K : nullptr, acc != nullptr ? acc + t * H : nullptr,
+        [&](int64_t G, const uint16_t* b) {
+          if (folded != nullptr) std::memcpy(folded + G * H, b, (size_t)H * 2);
+        });
+  }
+  return ST_OK;
+}
+
+int32_t orc_combine_prologue_rows(int32_t n, int32_t K, int32_t H, int32_t NvS,
+                                  const int32_t* dst_tok, int64_t M, const int64_t* rows,
+                                  const uint16_t* yrows, const float* wrows, int32_t weighted,
+                                  uint16_t* out, float* wsk_out, double* acc,
+                                  uint16_t* folded_rows) {
+  if (weighted && wrows == nullptr) return ST_INVALID;
+  auto find = [&](int64_t G) -> int64_t {
+    const int64_t* p = std::lower_bound(rows, rows + M, G);
+    return (p != rows + M && *p == G) ? (int64_t)(p - rows) : -1;
+  };
+  for (int64_t t = 0; t < n; ++t)
+    for (int k = 0; k < K; ++k)
+      if (find(decode_row(dst_tok[t * K + k])) < 0) return ST_INVALID;
+  if (folded_rows != nullptr) std::memcpy(folded_rows, yrows, (size_t)M * H * 2);
+  for (int64_t t = 0; t < n; ++t) {
+    combine_token_prologue(
+        K, H, NvS, dst_tok + t * K, [&](int64_t G) { return yrows + find(G) * H; },
+        [&](int64_t G) { return wrows != nullptr ? wrows[find(G)] : 0.0f; }, weighted,
+        out + t * H, wsk_out != nullptr ? wsk_out + t * K : nullptr,
+        acc != nullptr ? acc + t * H : nullptr, [&](int64_t G, const uint16_t* b) {
+          if (folded_rows != nullptr) std::memcpy(folded_rows + find(G) * H, b, (size_t)H * 2);
+        });
   }
   return ST_OK;
 }

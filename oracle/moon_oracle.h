@@ -91,6 +91,25 @@ int32_t orc_combine_rows(int32_t n, int32_t K, int32_t H, const int32_t* dst_tok
                          const float* wrows, int32_t weighted,
                          uint16_t* out, float* wsk_out, double* acc);
 
+/* Combine with the duplicate prologue: for every token and destination rank
+ * holding m >= 2 of its routes, the m rows are first summed in fp32
+ * (ascending k, c_k = w_nvs[row] when weighted, else 1) and rounded to bf16
+ * into the primary row; the main sum then takes primary routes only, a
+ * folded primary with coefficient 1, in float64, rounded once.  folded
+ * (may be NULL) [R*NvS,H] receives y with the folded primary rows. */
+int32_t orc_combine_prologue(int32_t R, int32_t K, int32_t S, int32_t H, int32_t NvS,
+                             const int32_t* dst, const uint16_t* y, const float* wnvs,
+                             int32_t weighted, uint16_t* out, float* wsk_out, double* acc,
+                             uint16_t* folded);
+
+/* The same for n sampled tokens, like orc_combine_rows; folded_rows [M,H]
+ * receives yrows with the folded primary rows. */
+int32_t orc_combine_prologue_rows(int32_t n, int32_t K, int32_t H, int32_t NvS,
+                                  const int32_t* dst_tok, int64_t M, const int64_t* rows,
+                                  const uint16_t* yrows, const float* wrows, int32_t weighted,
+                                  uint16_t* out, float* wsk_out, double* acc,
+                                  uint16_t* folded_rows);
+
 /* Prefetch index: out [R,B,2] = (owner rank, rank-local row) or (-1,-1). */
 int32_t orc_prefetch_index(int32_t R, int32_t E, int32_t B, const int32_t* etc, int32_t* out);
 

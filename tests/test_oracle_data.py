@@ -22,6 +22,19 @@ def _rand_bf16(rng, shape):
     return _bits(rng.standard_normal(shape).astype(np.float32))
 
 
+def _assert_nearest_bf16(out, acc):
+    """No bf16 bit neighbour of out is closer to acc.  Stepping past +-0 or
+    the largest finite value gives a NaN pattern, which is no competitor."""
+    o = _f32(out).astype(np.float64).reshape(-1)
+    a = np.asarray(acc, np.float64).reshape(-1)
+    ob = np.asarray(out).reshape(-1).astype(np.int64)
+    up = _f32(((ob + 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    dn = _f32(((ob - 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    d_up = np.nan_to_num(np.abs(up - a), nan=np.inf)
+    d_dn = np.nan_to_num(np.abs(dn - a), nan=np.inf)
+    assert (np.abs(o - a) <= d_up).all() and (np.abs(o - a) <= d_dn).all()
+
+
 CASES = [
     # R, E, K, S, B, P, H, skew
     (1, 4, 2, 8, 4, 4, 16, 0.0),
@@ -119,12 +132,7 @@ def test_weighted_combine_brute_force(case):
     assert np.allclose(acc.reshape(R * S, H), ref, rtol=1e-12, atol=1e-12)
     assert (wsk.view(np.uint32) == w.view(np.uint32)).all()
     # out is the nearest bf16 to acc: no neighbour is closer
-    o = _f32(out).astype(np.float64).reshape(-1)
-    a = acc.reshape(-1)
-    ob = out.reshape(-1).astype(np.int64)
-    up = _f32(((ob + 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
-    dn = _f32(((ob - 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
-    assert (np.abs(o - a) <= np.abs(up - a)).all() and (np.abs(o - a) <= np.abs(dn - a)).all()
+    _assert_nearest_bf16(out, acc)
 
 
 def test_combine_rows_matches_full_combine():
@@ -180,3 +188,128 @@ def test_prefetch_index_splits_expert_ids():
     owner, local = idx[..., 0][used], idx[..., 1][used]
     assert (owner * Eg + local == etc[used]).all()
     assert ((0 <= local) & (local < Eg)).all() and ((0 <= owner) & (owner < R)).all()
+
+
+# ---- combine with the duplicate prologue -------------------------------------
+
+def _prologue_brute_force(pl, y, wwin, weighted):
+    """Fold driven by the plan's duplicate records (the pages' structure): per
+    record, primary then its duplicate rows, fp32 separate multiply and add
+    (numpy float32), rounded by torch; then a route-major float64 sum over
+    primary routes, folded primaries with coefficient 1."""
+    R, S, K, NvS = pl.R, pl.S, pl.K, pl.NvS
+    H = y.shape[1]
+    folded = y.copy()
+    is_folded = np.zeros(R * NvS, bool)
+    for u in range(R):
+        for j in range(int(pl.dup_counts[u, 0])):
+            prow, lb, m = (int(v) for v in pl.dup_groups[u, j])
+            rows = [u * NvS + prow] + [u * NvS + int(pl.dup_loffs[u, lb + i]) for i in range(m)]
+            a = np.zeros(H, np.float32)
+            for G in rows:
+                c = np.float32(wwin[G]) if weighted else np.float32(1.0)
+                a = (a + (c * _f32(y[G])).astype(np.float32)).astype(np.float32)
+            folded[rows[0]] = _bits(a)
+            is_folded[rows[0]] = True
+    acc = np.zeros((R * S, H), np.float64)
+    dst = pl.dst.reshape(R * S, K)
+    for t in range(R * S):
+        for k in range(K):
+            d = int(dst[t, k])
+            if d < 0:
+                continue
+            if is_folded[d]:
+                acc[t] += _f32(folded[d]).astype(np.float64)
+            else:
+                c = np.float64(wwin[d]) if weighted else 1.0
+                acc[t] += c * _f32(y[d]).astype(np.float64)
+    return folded, is_folded, acc
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("weighted", [True, False])
+def test_prologue_combine_against_duplicate_records(case, weighted):
+    R, E, K, S, B, P, H, skew = case
+    rng = np.random.default_rng(R * 17 + K + int(weighted))
+    topk = rand_topk(rng, R, S, K, E, distinct=K <= E, skew=skew)
+    w = rng.random((R, S, K)).astype(np.float32)
+    pl = oracle.plan(topk, E, B, P)
+    y = _rand_bf16(rng, (R * pl.NvS, H))
+    _, wwin = oracle.dispatch(pl, np.zeros((R, S, H), np.uint16), w)
+    out, wsk, acc, folded = oracle.combine_prologue(pl, y, wwin, weighted=weighted)
+    f_ref, is_f, acc_ref = _prologue_brute_force(pl, y, wwin, weighted)
+    assert int(is_f.sum()) == int(pl.dup_counts[:, 0].sum())
+    assert (folded == f_ref).all()
+    assert (acc.reshape(R * S, H) == acc_ref).all()
+    # out is the nearest bf16 to acc
+    _assert_nearest_bf16(out, acc)
+    assert (wsk.view(np.uint32) == w.view(np.uint32)).all()
+
+
+def test_prologue_unweighted_power_of_two_groups_is_k_times_x():
+    """K = 4 over 4 ranks of 4 experts; every token splits its routes over
+    ranks in groups of 1, 2 or 4, the ranks shifted cyclically so that every
+    rank's load is exactly S*K and nothing moves to a slot.  Folding m copies
+    of x gives m*x exactly (m a power of two, so the bf16 rounding of the fold
+    is exact), the outer sum is exact, so out = 4x exactly."""
+    rng = np.random.default_rng(21)
+    R, E, K, S, B, P, H = 4, 16, 4, 24, 4, 4, 32
+    patterns = [(1, 1, 1, 1), (2, 1, 1), (2, 2), (4,)]
+    topk = np.empty((R * S, K), np.int32)
+    for t in range(R * S):
+        sizes, shift = patterns[(t // R) % len(patterns)], t % R
+        row = []
+        for j, m in enumerate(sizes):
+            rk = (shift + j) % R
+            row += list(rk * 4 + rng.permutation(4)[:m])
+        topk[t] = rng.permutation(np.array(row))
+    topk = topk.reshape(R, S, K)
+    hidden = _rand_bf16(rng, (R, S, H))
+    pl = oracle.plan(topk, E, B, P)
+    assert pl.status == oracle.OK and int(pl.dup_counts[:, 0].sum()) > 0
+    assert int(pl.remote_stats.sum()) == 0
+    win, _ = oracle.dispatch(pl, hidden, None)
+    out, _, acc, folded = oracle.combine_prologue(pl, win, None, weighted=False)
+    assert (acc == K * _f32(hidden).astype(np.float64)).all()
+    assert (out == _bits(K * _f32(hidden))).all()
+
+
+def test_prologue_without_duplicates_equals_plain_combine():
+    """Every token's K routes on K distinct ranks, shifted cyclically so that
+    every rank's load is exactly S*K and nothing moves to a slot: nothing to
+    fold, so the prologue variant is the plain combine, bit for bit."""
+    rng = np.random.default_rng(22)
+    R, E, K, S, B, P, H = 4, 16, 3, 20, 4, 4, 24
+    topk = np.empty((R * S, K), np.int32)
+    for t in range(R * S):
+        ranks = (t + np.arange(K)) % R
+        topk[t] = rng.permutation(ranks * 4 + rng.integers(0, 4, size=K))
+    topk = topk.reshape(R, S, K)
+    w = rng.random((R, S, K)).astype(np.float32)
+    pl = oracle.plan(topk, E, B, P)
+    assert int(pl.dup_counts.sum()) == 0 and int(pl.remote_stats.sum()) == 0
+    y = _rand_bf16(rng, (R * pl.NvS, H))
+    _, wwin = oracle.dispatch(pl, np.zeros((R, S, H), np.uint16), w)
+    o1, w1, a1 = oracle.combine(pl, y, wwin, weighted=True)
+    o2, w2, a2, f2 = oracle.combine_prologue(pl, y, wwin, weighted=True)
+    assert (o1 == o2).all() and (a1 == a2).all() and (w1 == w2).all() and (f2 == y).all()
+
+
+def test_prologue_rows_matches_full():
+    rng = np.random.default_rng(23)
+    R, E, K, S, B, P, H = 3, 12, 4, 20, 4, 4, 24
+    topk = rand_topk(rng, R, S, K, E, skew=1.0)
+    w = rng.random((R, S, K)).astype(np.float32)
+    pl = oracle.plan(topk, E, B, P)
+    y = _rand_bf16(rng, (R * pl.NvS, H))
+    _, wwin = oracle.dispatch(pl, np.zeros((R, S, H), np.uint16), w)
+    out, wsk, acc, folded = oracle.combine_prologue(pl, y, wwin, weighted=True)
+    toks = np.array([0, 3, 17, 31, R * S - 1])
+    dst_tok = pl.dst.reshape(R * S, K)[toks]
+    rows = np.unique(pc.decode(dst_tok).reshape(-1))
+    o2, w2, a2, f2 = oracle.combine_prologue_rows(dst_tok, rows, y[rows], pl.NvS, wwin[rows],
+                                                  weighted=True)
+    assert (o2 == out.reshape(R * S, H)[toks]).all()
+    assert (a2 == acc.reshape(R * S, H)[toks]).all()
+    assert (w2 == wsk.reshape(R * S, K)[toks]).all()
+    assert (f2 == folded[rows]).all()
