@@ -136,6 +136,57 @@ def run_steps(moon, ctx, sets, steps, warmup, stream):
     return ms_step, wall, calls
 
 
+def time_call(fn, iters, stream):
+    """Average microseconds of `fn` over `iters` back-to-back calls (HIP events on `stream`)."""
+    import torch
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e3
+
+
+def measure_ablations(moon, ctx, s, nb, stream, iters):
+    """The two one-GPU variants of the pages' deduplication on the same input:
+    dispatch writing duplicates from registers (no epilogue re-read) and combine
+    with the duplicate prologue (folds into the window, then gathers primaries)."""
+    c = ctx.cfg
+    row = 2 * c.H
+    win, wwin = moon.window_tensors(ctx)
+    t_fused = time_call(lambda: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w,
+                                                   flags=moon.MOON_DISPATCH_FUSED_DUPS,
+                                                   stream=stream), iters, stream)
+    t_epi = time_call(lambda: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream),
+                      iters, stream)
+    flags = moon.MOON_COMBINE_WEIGHTED | moon.MOON_COMBINE_DUP_PROLOGUE
+    t_pro = time_call(lambda: moon.moon_combine(ctx, s.plan, s.y, wwin, flags, s.out, s.wsk,
+                                                stream=stream), iters, stream)
+    t_plain = time_call(lambda: moon.moon_combine(ctx, s.plan, s.y, wwin,
+                                                  moon.MOON_COMBINE_WEIGHTED, s.out, s.wsk,
+                                                  stream=stream), iters, stream)
+    # prologue: every group reads its m+1 rows (and weights) and writes one
+    # folded row; the gather then reads one row per primary route
+    pro_bytes = (row * (nb["n_grp"] + nb["n_dup"]) + 4 * (nb["n_grp"] + nb["n_dup"])
+                 + 12 * nb["n_grp"] + 4 * nb["n_dup"] + row * nb["n_grp"]
+                 + row * (nb["n_route"] - nb["n_dup"]) + row * c.R * c.S + 4 * nb["n_route"] * 3)
+    moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream)  # restore the windows
+    return {
+        "dispatch_epilogue_us": round(t_epi, 2),
+        "dispatch_fused_dups_us": round(t_fused, 2),
+        "dispatch_fused_dups_GBps": round(nb["dispatch_minimal"] / (t_fused * 1e-6) / 1e9, 1),
+        "combine_plain_us": round(t_plain, 2),
+        "combine_dup_prologue_us": round(t_pro, 2),
+        "combine_dup_prologue_bytes": int(pro_bytes),
+        "combine_dup_prologue_GBps": round(pro_bytes / (t_pro * 1e-6) / 1e9, 1),
+        "dup_groups": nb["n_grp"], "dup_rows": nb["n_dup"],
+    }
+
+
 def source_hash(files):
     h = hashlib.sha256()
     for f in files:
@@ -401,6 +452,8 @@ def main():
                          "algorithmic_bytes_per_call": int(disp_bytes),
                          "avg_call_us": round(calls["dispatch"], 2)}
 
+    ablations = measure_ablations(moon, ctx, sets[0], nb, stream, max(10, args.steps // 2))
+
     sweep = []
     if not args.no_sweep and config == 2:
         # maxvio sweep on the same shapes: level "0" is this workload's routing,
@@ -457,6 +510,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "dispatch_roofline": dispatch_roofline,
+        "ablations": ablations,
         "cpu_baseline": cpu,
     }
     for s in sets:

@@ -34,6 +34,7 @@ MOON_ERR_INTERNAL = -11
 
 MOON_COMBINE_WEIGHTED = 0x1
 MOON_DISPATCH_FUSED_DUPS = 0x2
+MOON_COMBINE_DUP_PROLOGUE = 0x4
 
 _i32, _u32, _vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
 

@@ -367,14 +367,18 @@ moon_status moon_combine(moon_ctx* ctx, const moon_comm_plan* plan, const void* 
   if (!ctx_ok(ctx) || !plan_ok(plan) || y_nvsh == nullptr || out_rsh == nullptr)
     return MOON_ERR_INVALID_ARG;
   if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
-  if ((flags & ~MOON_COMBINE_WEIGHTED) != 0) return MOON_ERR_INVALID_ARG;
+  if ((flags & ~(MOON_COMBINE_WEIGHTED | MOON_COMBINE_DUP_PROLOGUE)) != 0)
+    return MOON_ERR_INVALID_ARG;
   const bool weighted = (flags & MOON_COMBINE_WEIGHTED) != 0;
+  // the prologue folds into the persistent shard: the context's hidden window
+  uint16_t* fold = (flags & MOON_COMBINE_DUP_PROLOGUE) != 0
+                       ? static_cast<uint16_t*>(ctx->hidden_win) : nullptr;
   if ((weighted || w_rsk_out != nullptr) && w_nvs == nullptr) return MOON_ERR_INVALID_ARG;
   if (!aligned(y_nvsh, 16) || !aligned(out_rsh, 16) || !aligned(w_nvs, 4) || !aligned(w_rsk_out, 4))
     return MOON_ERR_INVALID_ARG;
   DeviceGuard g(ctx->device);
   if (moon::launch_combine(ctx->d, plan->a, static_cast<const uint16_t*>(y_nvsh), w_nvs, weighted,
-                           static_cast<uint16_t*>(out_rsh), w_rsk_out, stream) != hipSuccess)
+                           fold, static_cast<uint16_t*>(out_rsh), w_rsk_out, stream) != hipSuccess)
     return MOON_ERR_HIP;
   return MOON_OK;
 }

@@ -92,9 +92,11 @@ hipError_t launch_plan(const Dims& d, const Scratch& sc, const PlanArrays& pa, c
                        const int32_t* tpe, hipStream_t s);
 hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* hidden,
                            const float* w, uint16_t* win, float* wwin, bool fused, hipStream_t s);
+// fold != NULL selects the duplicate prologue; folded primary rows are
+// written there ([R*NvS, H], the context window).
 hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y,
-                          const float* wnvs, bool weighted, uint16_t* out, float* wsk,
-                          hipStream_t s);
+                          const float* wnvs, bool weighted, uint16_t* fold, uint16_t* out,
+                          float* wsk, hipStream_t s);
 // 16-byte vector of raw bits (eight bf16 values).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

@@ -66,6 +66,16 @@ typedef enum {
 
 /* Combine flag: scale each routed row by the route weight stored at its row. */
 #define MOON_COMBINE_WEIGHTED 0x1u
+/* Combine flag: duplicate prologue (Guide, Buffer.combine).  Before the
+ * gather, for every token and destination rank holding m >= 2 of its routes,
+ * the m rows are summed in fp32 (ascending k, c_k * y with a separate
+ * multiply and add, c_k as for the gather) and the bf16 result (nearest,
+ * ties to even) is stored at the primary's row of the context's hidden
+ * window, the persistent local shard; y_nvsh itself is written only when it
+ * is that window.  The gather then adds folded primaries with coefficient 1
+ * and skips duplicates.  The window's dispatched rows at those primaries are
+ * overwritten. */
+#define MOON_COMBINE_DUP_PROLOGUE 0x4u
 /* Dispatch flag: write duplicate rows from registers in the scatter kernel
  * instead of expanding them in the epilogue (same result). */
 #define MOON_DISPATCH_FUSED_DUPS 0x2u
@@ -159,7 +169,8 @@ moon_status moon_dispatch(moon_ctx* ctx, const moon_comm_plan* plan, const void*
 
 /* Combine (Guide, Buffer.combine): out_rsh[r][s] = bf16(sum over k of
  * c_k * y[row(r,s,k)]) accumulated in fp32 in ascending k, c_k = w_nvs[row]
- * with MOON_COMBINE_WEIGHTED, else 1.  y_nvsh [R*NvS,H] bf16 (may be the
+ * with MOON_COMBINE_WEIGHTED, else 1; flags may add
+ * MOON_COMBINE_DUP_PROLOGUE.  y_nvsh [R*NvS,H] bf16 (may be the
  * context window); w_nvs [R*NvS] fp32, required when weighted or when
  * w_rsk_out is given; w_rsk_out [R,S,K] (optional) receives the route
  * weights gathered back through the same dst encoding. */
