@@ -38,9 +38,12 @@ def _load(path=None):
         return _bind(ctypes.CDLL(path))
     if _lib is None:
         # A planted-mistake build may stand in for the oracle in the mutation test.
-        so = os.environ.get("MOON_ORACLE_SO", _SO)
-        if not os.path.exists(so):
-            build(out=so)
+        so = os.environ.get("MOON_ORACLE_SO")
+        if so is None:
+            so = _SO
+            # rebuild when the source is newer than the library
+            if not os.path.exists(so) or os.path.getmtime(so) < os.path.getmtime(_SRC):
+                build(out=so)
         _lib = _bind(ctypes.CDLL(so))
     return _lib
 
@@ -68,6 +71,10 @@ def _bind(lib):
     lib.orc_combine_prologue_rows.restype = i32
     lib.orc_prefetch_index.argtypes = [i32, i32, i32, vp, vp]
     lib.orc_prefetch_index.restype = i32
+    lib.orc_prefetch_weight.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.orc_prefetch_weight.restype = i32
+    lib.orc_reduce_grad.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.orc_reduce_grad.restype = i32
     lib.orc_bf16_from_double.argtypes = [ctypes.c_double]
     lib.orc_bf16_from_double.restype = ctypes.c_uint16
     return lib
@@ -250,6 +257,46 @@ def combine_prologue_rows(dst_tok, rows, yrows, NvS, wrows=None, weighted=True, 
     if st != OK:
         raise RuntimeError(f"orc_combine_prologue_rows status {st}")
     return out, wsk, acc, folded
+
+
+def _ptr_array(arrs):
+    return (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+
+
+def prefetch_weight(etc, E, experts, slots):
+    """Weight prefetch.  etc [R,B] int32; experts: list of [E, ...] arrays;
+    slots: list of [R, B, ...] arrays of the same dtypes, updated in place
+    (and returned)."""
+    etc = _c(etc, np.int32)
+    R, B = etc.shape
+    experts = [np.ascontiguousarray(x) for x in experts]
+    for x, sl in zip(experts, slots):
+        assert sl.flags.c_contiguous and sl.dtype == x.dtype and sl.shape[:2] == (R, B)
+        assert x.shape[0] == E and sl.shape[2:] == x.shape[1:]
+    rb = np.array([x[0].nbytes if E else 0 for x in experts], np.int64)
+    st = _load().orc_prefetch_weight(R, E, B, _p(etc), len(experts), _ptr_array(experts),
+                                     _ptr_array(slots), _p(rb))
+    if st != OK:
+        raise RuntimeError(f"orc_prefetch_weight status {st}")
+    return slots
+
+
+def reduce_grad(etc, E, grads, slot_grads):
+    """Gradient reduction.  etc [R,B] int32; grads: list of [E, ...] float32
+    arrays; slot_grads: list of [R, B, ...] float32 arrays; both updated in
+    place (and returned)."""
+    etc = _c(etc, np.int32)
+    R, B = etc.shape
+    for g, sg in zip(grads, slot_grads):
+        assert g.flags.c_contiguous and sg.flags.c_contiguous
+        assert g.dtype == np.float32 and sg.dtype == np.float32
+        assert g.shape[0] == E and sg.shape[:2] == (R, B) and sg.shape[2:] == g.shape[1:]
+    le = np.array([g[0].size if E else 0 for g in grads], np.int64)
+    st = _load().orc_reduce_grad(R, E, B, _p(etc), len(grads), _ptr_array(grads),
+                                 _ptr_array(slot_grads), _p(le))
+    if st != OK:
+        raise RuntimeError(f"orc_reduce_grad status {st}")
+    return grads, slot_grads
 
 
 def prefetch_index(pl):

@@ -9,9 +9,14 @@
 //               weight to its row, zero the padding (same page, Buffer.dispatch)
 //   combine   = per token, sum the K routed rows (weighted or not) back into
 //               token-major order (same page, Buffer.combine)
-//   prefetch  = split a slot's expert id into (owner rank, local row)
+//   prefetch  = split a slot's expert id into (owner rank, local row) and
+//               copy that expert's weight rows into the slot
 //               (same page, Buffer.prefetch_weight)
-// Arithmetic on values happens only in combine, in float64.
+//   reduce    = add every slot gradient back into its expert's gradient row
+//               and clear the consumed slots (same page, Buffer.reduce_grad)
+// Arithmetic on values happens in combine (float64, the duplicate prologue's
+// fold in float32) and in the gradient reduction (float32, as the pages'
+// gradient tensors are).
 
 #include "moon_oracle.h"
 
@@ -526,6 +531,64 @@ int32_t orc_prefetch_index(int32_t R, int32_t E, int32_t B, const int32_t* etc, 
     int32_t e = etc[j];
     out[j * 2 + 0] = e >= 0 ? e / Eg : -1;
     out[j * 2 + 1] = e >= 0 ? e % Eg : -1;
+  }
+  return ST_OK;
+}
+
+// Weight prefetch (Visual Guide, Buffer.prefetch_weight): every used slot j
+// of rank u receives a copy of the weights of expert experts_to_copy[u][j],
+// taken from the authoritative expert rows [0, E); a -1 slot is left as it
+// is.  The copy moves bytes, so it is the same for bf16, fp32 or packed
+// formats.  The tensors (gate, up, down and optional scales) are treated one
+// after another.  experts[t] is [E, row_bytes[t]], slots[t] is
+// [R, B, row_bytes[t]].
+int32_t orc_prefetch_weight(int32_t R, int32_t E, int32_t B, const int32_t* etc, int32_t n,
+                            const uint8_t* const* experts, uint8_t* const* slots,
+                            const int64_t* row_bytes) {
+  for (int t = 0; t < n; ++t) {
+    for (int u = 0; u < R; ++u) {
+      for (int j = 0; j < B; ++j) {
+        int32_t e = etc[u * B + j];
+        if (e < 0) continue;
+        if (e >= E) return ST_INVALID;
+        uint8_t* dst = slots[t] + ((int64_t)u * B + j) * row_bytes[t];
+        std::memcpy(dst, experts[t] + (int64_t)e * row_bytes[t], (size_t)row_bytes[t]);
+      }
+    }
+  }
+  return ST_OK;
+}
+
+// Gradient reduction (Visual Guide, Buffer.reduce_grad): for every expert e
+// (each owner handles its own experts), the accumulator starts from the
+// authoritative gradient row e, then adds the slot gradients of every slot
+// that held e, visiting ranks in ascending order (on one rank e occupies at
+// most one slot; slots ascending if it were more), in fp32 as the gradient
+// tensors are fp32 (a plain a + b per element).  The sum is written back to
+// row e, and every consumed slot (every used slot) is cleared to +0.0.
+// Experts that no slot held keep their row unchanged.  grads[t] is
+// [E, row_elems[t]], slot_grads[t] is [R, B, row_elems[t]].
+int32_t orc_reduce_grad(int32_t R, int32_t E, int32_t B, const int32_t* etc, int32_t n,
+                        float* const* grads, float* const* slot_grads, const int64_t* row_elems) {
+  for (int i = 0; i < R * B; ++i)
+    if (etc[i] >= E) return ST_INVALID;
+  for (int t = 0; t < n; ++t) {
+    const int64_t L = row_elems[t];
+    for (int e = 0; e < E; ++e) {
+      float* g = grads[t] + (int64_t)e * L;
+      for (int u = 0; u < R; ++u) {
+        for (int j = 0; j < B; ++j) {
+          if (etc[u * B + j] != e) continue;
+          const float* sg = slot_grads[t] + ((int64_t)u * B + j) * L;
+          for (int64_t x = 0; x < L; ++x) g[x] = g[x] + sg[x];
+        }
+      }
+    }
+    for (int u = 0; u < R; ++u)
+      for (int j = 0; j < B; ++j)
+        if (etc[u * B + j] >= 0)
+          std::fill(slot_grads[t] + ((int64_t)u * B + j) * L,
+                    slot_grads[t] + ((int64_t)u * B + j + 1) * L, 0.0f);
   }
   return ST_OK;
 }

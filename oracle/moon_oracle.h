@@ -10,7 +10,7 @@
  *
  * What it computes follows the "MoonEP Public API Visual Guide"
  * (sections Buffer.dispatch, Buffer.combine, Buffer.prefetch_weight,
- * MoonEPCommPlan) and the MoonEP README (Performance: maxvio equation;
+ * Buffer.reduce_grad, MoonEPCommPlan) and the MoonEP README (Performance: maxvio equation;
  * Integration: How to set B).  Where the pages state only guarantees
  * (perfect balance, slot experts from one remote home rank) the oracle takes
  * one deterministic reading, written out in the .cpp next to each step.
@@ -112,6 +112,19 @@ int32_t orc_combine_prologue_rows(int32_t n, int32_t K, int32_t H, int32_t NvS,
 
 /* Prefetch index: out [R,B,2] = (owner rank, rank-local row) or (-1,-1). */
 int32_t orc_prefetch_index(int32_t R, int32_t E, int32_t B, const int32_t* etc, int32_t* out);
+
+/* Weight prefetch for n tensors: slots[t] [R,B,row_bytes[t]] bytes, slot
+ * (u,j) <- experts[t] row etc[u][j] ([E,row_bytes[t]]); unused slots keep
+ * their bytes. */
+int32_t orc_prefetch_weight(int32_t R, int32_t E, int32_t B, const int32_t* etc, int32_t n,
+                            const uint8_t* const* experts, uint8_t* const* slots,
+                            const int64_t* row_bytes);
+
+/* Gradient reduction for n fp32 tensors: grads[t] [E,L] row e <- row e +
+ * slot gradients of the slots holding e (ranks ascending, fp32 adds);
+ * slot_grads[t] [R,B,L] used slots <- 0. */
+int32_t orc_reduce_grad(int32_t R, int32_t E, int32_t B, const int32_t* etc, int32_t n,
+                        float* const* grads, float* const* slot_grads, const int64_t* row_elems);
 
 /* Nearest bf16 (ties to even) of a double, as bits.  Exposed for tests. */
 uint16_t orc_bf16_from_double(double v);

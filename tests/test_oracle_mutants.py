@@ -36,9 +36,22 @@ MUTANTS = {
                               "return d >= 0 ? (int64_t)d : -(int64_t)d;"),
     "rounding_truncates": ("double r = std::nearbyint(scaled);", "double r = std::trunc(scaled);"),
     "remote_stats_counts_all_slots": ("if (etc[(size_t)u * B + j] >= 0) {", "if (true) {"),
+    "prologue_fold_drops_weight": ("float c = weighted ? wat(Gm) : 1.0f;", "float c = 1.0f;"),
+    "prefetch_copies_neighbour_expert": ("std::memcpy(dst, experts[t] + (int64_t)e * row_bytes[t],",
+                                         "std::memcpy(dst, experts[t] + (int64_t)(e ^ 1) * "
+                                         "row_bytes[t],"),
+    "prefetch_slot_index_transposed": ("uint8_t* dst = slots[t] + ((int64_t)u * B + j) * row_bytes[t];",
+                                       "uint8_t* dst = slots[t] + ((int64_t)j * R + u) * row_bytes[t];"),
+    "reduce_grad_ranks_descending": ("      for (int u = 0; u < R; ++u) {\n        for (int j = 0; j < B; ++j) {\n"
+                                     "          if (etc[u * B + j] != e) continue;",
+                                     "      for (int u = R - 1; u >= 0; --u) {\n        for (int j = 0; j < B; ++j) {\n"
+                                     "          if (etc[u * B + j] != e) continue;"),
+    "reduce_grad_keeps_slots": ("        if (etc[u * B + j] >= 0)\n          std::fill(",
+                                "        if (etc[u * B + j] >= 1 << 30)\n          std::fill("),
+    "reduce_grad_overwrites_seed": ("g[x] = g[x] + sg[x];", "g[x] = sg[x];"),
 }
 
-PIN_TESTS = ["tests/test_oracle_plan.py", "tests/test_oracle_data.py"]
+PIN_TESTS = ["tests/test_oracle_plan.py", "tests/test_oracle_data.py", "tests/test_oracle_weights.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -52,7 +65,8 @@ def test_mutant_is_caught(name, tmp_path):
     (mdir / "moon_oracle.cpp").write_text(src.replace(old, new))
     (mdir / "moon_oracle.h").write_text(open(os.path.join(ROOT, "oracle", "moon_oracle.h")).read())
     so = str(mdir / "liboracle_mutant.so")
-    subprocess.run(["g++", "-std=c++17", "-O1", "-shared", "-fPIC", str(mdir / "moon_oracle.cpp"),
+    subprocess.run(["g++", "-std=c++17", "-O1", "-ffp-contract=off", "-shared", "-fPIC",
+                    str(mdir / "moon_oracle.cpp"),
                     "-o", so], check=True)
     env = dict(os.environ, MOON_ORACLE_SO=so)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
