@@ -187,6 +187,48 @@ def measure_ablations(moon, ctx, s, nb, stream, iters):
     }
 
 
+# Expert FFN intermediate width H' per workload: DeepSeek-V3's expert width for
+# the DSv3-shaped workload; H/2 (a reading: the pages give none) for r8-e64-k6.
+FFN_WIDTH = {2: 1024, 3: 2048}
+
+
+def measure_weights(moon, ctx, s, stream, iters, hp):
+    """Weight prefetch and gradient reduction for the plan of `s`: gate, up and
+    down tensors [E, H*H'] (bf16 weights, fp32 gradients) and their slots."""
+    import torch
+    import synth
+    import synth.gpu as sg
+    c = ctx.cfg
+    L = c.H * hp
+    pt = moon.plan_tensors(s.plan)
+    etc = pt["experts_to_copy"].cpu()
+    n_used = int((etc >= 0).sum())
+    n_held = int(torch.unique(etc[etc >= 0]).numel())
+    key = synth.stream_key(12345, 21)
+    w = [sg.fill_bf16(torch.empty((c.E, L), dtype=torch.bfloat16, device="cuda"), key, i * c.E * L)
+         for i in range(3)]
+    sl = [torch.zeros((c.R, ctx.B, L), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    t_pw = time_call(lambda: moon.moon_prefetch_weight(ctx, s.plan, w, sl, stream=stream), iters,
+                     stream)
+    del w, sl
+    g = [sg.fill_bf16(torch.empty((c.E, L), dtype=torch.bfloat16, device="cuda"), key).float()
+         for _ in range(3)]
+    sgr = [torch.zeros((c.R, ctx.B, L), dtype=torch.float32, device="cuda") for _ in range(3)]
+    t_rg = time_call(lambda: moon.moon_reduce_grad(ctx, s.plan, g, sgr, stream=stream), iters,
+                     stream)
+    del g, sgr
+    torch.cuda.empty_cache()
+    pw_bytes = 3 * n_used * L * 2 * 2          # read the expert row, write the slot
+    rg_bytes = 3 * (n_held + n_used) * L * 4 * 2  # expert row read+write; slot read+clear
+    return {
+        "ffn_width": hp, "tensors": 3, "slots_used": n_used, "experts_held": n_held,
+        "prefetch_weight_us": round(t_pw, 2), "prefetch_weight_bytes": pw_bytes,
+        "prefetch_weight_GBps": round(pw_bytes / (t_pw * 1e-6) / 1e9, 1),
+        "reduce_grad_us": round(t_rg, 2), "reduce_grad_bytes": rg_bytes,
+        "reduce_grad_GBps": round(rg_bytes / (t_rg * 1e-6) / 1e9, 1),
+    }
+
+
 def source_hash(files):
     h = hashlib.sha256()
     for f in files:
@@ -202,6 +244,7 @@ PMC_SOURCES = ["combine_balanced_planning_amd/csrc/moon_internal.h",
                "combine_balanced_planning_amd/csrc/moon_plan.hip",
                "combine_balanced_planning_amd/csrc/moon_dispatch.hip",
                "combine_balanced_planning_amd/csrc/moon_combine.hip",
+               "combine_balanced_planning_amd/csrc/moon_weights.hip",
                "synth/__init__.py"]
 
 
@@ -453,6 +496,9 @@ def main():
                          "avg_call_us": round(calls["dispatch"], 2)}
 
     ablations = measure_ablations(moon, ctx, sets[0], nb, stream, max(10, args.steps // 2))
+    log("[bench] weight prefetch and gradient reduction")
+    weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
+                              FFN_WIDTH[config])
 
     sweep = []
     if not args.no_sweep and config == 2:
@@ -511,6 +557,7 @@ def main():
         "roofline": roofline,
         "dispatch_roofline": dispatch_roofline,
         "ablations": ablations,
+        "weights": weights,
         "cpu_baseline": cpu,
     }
     for s in sets:

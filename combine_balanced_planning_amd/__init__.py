@@ -56,6 +56,14 @@ class moon_plan_arrays(ctypes.Structure):
                [(n, _i32) for n in ("N", "R", "E", "B", "NvS", "K")]
 
 
+class moon_weight_tensor(ctypes.Structure):
+    _fields_ = [("experts", _vp), ("slots", _vp), ("row_bytes", ctypes.c_int64)]
+
+
+class moon_grad_tensor(ctypes.Structure):
+    _fields_ = [("expert_grads", _vp), ("slot_grads", _vp), ("row_elems", ctypes.c_int64)]
+
+
 _P = ctypes.POINTER
 _lib.moon_ctx_create.argtypes = [_P(moon_config), _P(_vp)]
 _lib.moon_ctx_layout.argtypes = [_vp, _P(moon_layout)]
@@ -71,11 +79,13 @@ _lib.moon_plan.argtypes = [_vp, _vp, _vp, _vp, _vp]
 _lib.moon_dispatch.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _u32, _vp]
 _lib.moon_combine.argtypes = [_vp, _vp, _vp, _vp, _u32, _vp, _vp, _vp]
 _lib.moon_prefetch_index.argtypes = [_vp, _vp, _vp, _vp]
+_lib.moon_prefetch_weight.argtypes = [_vp, _vp, _P(moon_weight_tensor), _i32, _vp]
+_lib.moon_reduce_grad.argtypes = [_vp, _vp, _P(moon_grad_tensor), _i32, _vp]
 _lib.moon_status_str.argtypes = [_i32]
 _lib.moon_status_str.restype = ctypes.c_char_p
 for _f in ("moon_ctx_create", "moon_ctx_layout", "moon_plan_create", "moon_plan_clone",
            "moon_plan_view", "moon_plan_status", "moon_plan", "moon_dispatch", "moon_combine",
-           "moon_prefetch_index"):
+           "moon_prefetch_index", "moon_prefetch_weight", "moon_reduce_grad"):
     getattr(_lib, _f).restype = _i32
 
 
@@ -218,6 +228,50 @@ def moon_prefetch_index(ctx, plan, out, stream=None):
     _check(_lib.moon_prefetch_index(ctx.ptr, plan.ptr,
                                     _ptr(out, torch.int32, c.R * ctx.B * 2, "out"),
                                     _stream(stream)), "moon_prefetch_index")
+
+
+def _expert_pair(ctx, rows, slots, name, dtype=None):
+    """Check an ([E, ...], [R, B, ...]) tensor pair; returns (ptrs, row elements)."""
+    c = ctx.cfg
+    for t, what in ((rows, f"{name} rows"), (slots, f"{name} slots")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous CUDA tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if rows.dtype != slots.dtype:
+        raise ValueError(f"{name}: rows and slots differ in dtype")
+    if rows.shape[0] != c.E or tuple(slots.shape[:2]) != (c.R, ctx.B) or \
+            tuple(slots.shape[2:]) != tuple(rows.shape[1:]):
+        raise ValueError(f"{name}: expected rows [E={c.E}, ...] and slots [R={c.R}, B={ctx.B}, "
+                         f"...] of one row shape, got {tuple(rows.shape)} and "
+                         f"{tuple(slots.shape)}")
+    return _vp(rows.data_ptr()), _vp(slots.data_ptr()), rows[0].numel()
+
+
+def moon_prefetch_weight(ctx, plan, experts, slots, stream=None):
+    """experts: list of [E, ...] tensors (rows [0, E) of each weight tensor);
+    slots: list of [R, B, ...] tensors of the same dtypes, written in place."""
+    if len(experts) != len(slots):
+        raise ValueError("experts and slots must pair up")
+    arr = (moon_weight_tensor * max(len(experts), 1))()
+    for i, (x, sl) in enumerate(zip(experts, slots)):
+        px, ps, n = _expert_pair(ctx, x, sl, f"tensor {i}")
+        arr[i] = moon_weight_tensor(px, ps, n * x.element_size())
+    _check(_lib.moon_prefetch_weight(ctx.ptr, plan.ptr, arr, len(experts), _stream(stream)),
+           "moon_prefetch_weight")
+
+
+def moon_reduce_grad(ctx, plan, grads, slot_grads, stream=None):
+    """grads: list of [E, ...] float32 tensors (updated); slot_grads: list of
+    [R, B, ...] float32 tensors (used slots cleared)."""
+    if len(grads) != len(slot_grads):
+        raise ValueError("grads and slot_grads must pair up")
+    arr = (moon_grad_tensor * max(len(grads), 1))()
+    for i, (g, sg) in enumerate(zip(grads, slot_grads)):
+        pg, ps, n = _expert_pair(ctx, g, sg, f"gradient {i}", torch.float32)
+        arr[i] = moon_grad_tensor(pg, ps, n)
+    _check(_lib.moon_reduce_grad(ctx.ptr, plan.ptr, arr, len(grads), _stream(stream)),
+           "moon_reduce_grad")
 
 
 # ---------------------------------------------------------------------------

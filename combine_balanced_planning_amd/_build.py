@@ -5,7 +5,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SO = os.path.join(HERE, "libmoon.so")
-SOURCES = ["moon_api.hip", "moon_plan.hip", "moon_dispatch.hip", "moon_combine.hip"]
+SOURCES = ["moon_api.hip", "moon_plan.hip", "moon_dispatch.hip", "moon_combine.hip",
+           "moon_weights.hip"]
 
 # -ffp-contract=off keeps combine's multiply and add separate (no fused
 # multiply-add), so its rounding is the one the accumulation order defines.

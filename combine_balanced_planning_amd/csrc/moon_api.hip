@@ -193,6 +193,10 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   const size_t o_recv = carve(off, (size_t)d.R * 3 * i4);
   const size_t o_agg = carve(off, (size_t)d.ntiles * d.R * 8);
   const size_t o_epoch = carve(off, i4);
+  const size_t o_used = carve(off, (size_t)d.R * d.B * i4);
+  const size_t o_acte = carve(off, (size_t)d.E * i4);
+  const size_t o_actm = carve(off, (size_t)d.E * d.R * i4);
+  const size_t o_scnt = carve(off, 2 * i4);
   if (hipMalloc(&c->hidden_win, rows * d.H * 2) != hipSuccess ||
       hipMalloc(reinterpret_cast<void**>(&c->w_win), rows * 4) != hipSuccess ||
       hipMalloc(&c->scratch_mem, off) != hipSuccess) {
@@ -219,6 +223,10 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   c->sc.recv_cnt = c->sc.recv + 2 * d.R;
   c->sc.tile_agg = reinterpret_cast<uint64_t*>(b + o_agg);
   c->sc.epoch = reinterpret_cast<uint32_t*>(b + o_epoch);
+  c->si.used = reinterpret_cast<int32_t*>(b + o_used);
+  c->si.act_e = reinterpret_cast<int32_t*>(b + o_acte);
+  c->si.act_match = reinterpret_cast<int32_t*>(b + o_actm);
+  c->si.counts = reinterpret_cast<int32_t*>(b + o_scnt);
   *out = c;
   return MOON_OK;
 }
@@ -379,6 +387,59 @@ moon_status moon_combine(moon_ctx* ctx, const moon_comm_plan* plan, const void* 
   DeviceGuard g(ctx->device);
   if (moon::launch_combine(ctx->d, plan->a, static_cast<const uint16_t*>(y_nvsh), w_nvs, weighted,
                            fold, static_cast<uint16_t*>(out_rsh), w_rsk_out, stream) != hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
+moon_status moon_prefetch_weight(moon_ctx* ctx, const moon_comm_plan* plan,
+                                 const moon_weight_tensor* tensors, int32_t n_tensors,
+                                 hipStream_t stream) {
+  if (!ctx_ok(ctx) || !plan_ok(plan) || tensors == nullptr || n_tensors < 1 ||
+      n_tensors > moon::kMaxWeightTensors)
+    return MOON_ERR_INVALID_ARG;
+  if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
+  const void* src[moon::kMaxWeightTensors];
+  void* dst[moon::kMaxWeightTensors];
+  int64_t bytes[moon::kMaxWeightTensors];
+  for (int t = 0; t < n_tensors; ++t) {
+    const moon_weight_tensor& w = tensors[t];
+    if (w.experts == nullptr || w.slots == nullptr || w.row_bytes <= 0 || w.row_bytes % 16 != 0 ||
+        !aligned(w.experts, 16) || !aligned(w.slots, 16))
+      return MOON_ERR_INVALID_ARG;
+    src[t] = w.experts;
+    dst[t] = w.slots;
+    bytes[t] = w.row_bytes;
+  }
+  DeviceGuard g(ctx->device);
+  if (moon::launch_prefetch_weight(ctx->d, plan->a, ctx->si, n_tensors, src, dst, bytes, stream) !=
+      hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
+moon_status moon_reduce_grad(moon_ctx* ctx, const moon_comm_plan* plan,
+                             const moon_grad_tensor* tensors, int32_t n_tensors,
+                             hipStream_t stream) {
+  if (!ctx_ok(ctx) || !plan_ok(plan) || tensors == nullptr || n_tensors < 1 ||
+      n_tensors > moon::kMaxWeightTensors)
+    return MOON_ERR_INVALID_ARG;
+  if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
+  float* grads[moon::kMaxWeightTensors];
+  float* slots[moon::kMaxWeightTensors];
+  int64_t bytes[moon::kMaxWeightTensors];
+  for (int t = 0; t < n_tensors; ++t) {
+    const moon_grad_tensor& w = tensors[t];
+    if (w.expert_grads == nullptr || w.slot_grads == nullptr || w.row_elems <= 0 ||
+        w.row_elems % 4 != 0 || w.row_elems > (INT64_MAX / 4) || !aligned(w.expert_grads, 16) ||
+        !aligned(w.slot_grads, 16))
+      return MOON_ERR_INVALID_ARG;
+    grads[t] = w.expert_grads;
+    slots[t] = w.slot_grads;
+    bytes[t] = w.row_elems * 4;
+  }
+  DeviceGuard g(ctx->device);
+  if (moon::launch_reduce_grad(ctx->d, plan->a, ctx->si, n_tensors, grads, slots, bytes, stream) !=
+      hipSuccess)
     return MOON_ERR_HIP;
   return MOON_OK;
 }

@@ -54,6 +54,17 @@ struct Scratch {
   uint32_t* epoch;       // [1] tag of the latest planning call
 };
 
+// Slot index of a plan, rebuilt by every weight prefetch and gradient
+// reduction call (context scratch).
+struct SlotIndex {
+  int32_t* used;       // [R*B] used slots u*B+j, ascending
+  int32_t* act_e;      // [E] experts held by at least one slot, ascending
+  int32_t* act_match;  // [E][R] slot the i-th held expert occupies on rank u (-1)
+  int32_t* counts;     // [2] used slots, held experts
+};
+
+constexpr int kMaxWeightTensors = 8;  // tensors per prefetch / reduction call
+
 // Words exchanged between workgroups of one launch: a 16-bit call tag and two
 // 24-bit counts, so a reader knows when a word is current without fences.
 __device__ __forceinline__ uint64_t pack_word(uint32_t tag, uint32_t a, uint32_t b) {
@@ -75,6 +86,7 @@ struct moon_ctx {
   float* w_win;          // fp32 [R*NvS]
   void* scratch_mem;
   moon::Scratch sc;
+  moon::SlotIndex si;
 };
 
 struct moon_comm_plan {
@@ -103,5 +115,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int64_t dst_global_row(int32_t v) { return v >= 0 ? v : -(int64_t)v - 1; }
 
 hipError_t launch_prefetch_index(const Dims& d, const PlanArrays& pa, int32_t* out, hipStream_t s);
+// n tensors; row_bytes[t] is a multiple of 16 (reduction: fp32 rows).
+hipError_t launch_prefetch_weight(const Dims& d, const PlanArrays& pa, const SlotIndex& si, int n,
+                                  const void* const* experts, void* const* slots,
+                                  const int64_t* row_bytes, hipStream_t s);
+hipError_t launch_reduce_grad(const Dims& d, const PlanArrays& pa, const SlotIndex& si, int n,
+                              float* const* grads, float* const* slot_grads,
+                              const int64_t* row_bytes, hipStream_t s);
 
 }  // namespace moon

@@ -184,6 +184,57 @@ moon_status moon_combine(moon_ctx* ctx, const moon_comm_plan* plan, const void* 
 moon_status moon_prefetch_index(moon_ctx* ctx, const moon_comm_plan* plan, int32_t* src_rb2,
                                 hipStream_t stream);
 
+/* One tensor of the expert weight buffer for moon_prefetch_weight (Guide,
+ * Buffer.prefetch_weight; README, Weight buffer).  The pages give every rank
+ * one [E+B, H, H'] tensor per projection whose rows [0, E) are the owners'
+ * expert weights mapped on every rank and whose rows [E, E+B) are the rank's
+ * prefetch slots.  With the R ranks on one GPU the shared rows are one array
+ * and the slot rows of all ranks are another:
+ *   experts  [E, row_bytes]     rows [0, E), read only
+ *   slots    [R, B, row_bytes]  rank u's slot j at row u*B + j, written
+ * row_bytes is the byte size of one expert row (H*H'*2 for bf16; any packed
+ * format or block scales alike, the copy moves bytes), a positive multiple of
+ * 16; both pointers 16-byte aligned.  Caller-owned device memory. */
+typedef struct {
+  const void* experts;
+  void* slots;
+  int64_t row_bytes;
+} moon_weight_tensor;
+
+/* Weight prefetch (Guide, Buffer.prefetch_weight): for every tensor and every
+ * used slot j of every rank u, slots[u][j] <- experts[experts_to_copy[u][j]]
+ * (the expert id names its owning rank and rank-local row); unused (-1)
+ * slots are not written.  n_tensors in [1, 8]: gate, up, down and, when
+ * present, their scales.  Asynchronous on `stream`; uses context scratch, so
+ * the context's stream rule applies.  A plan whose device status is not OK
+ * writes nothing. */
+moon_status moon_prefetch_weight(moon_ctx* ctx, const moon_comm_plan* plan,
+                                 const moon_weight_tensor* tensors, int32_t n_tensors,
+                                 hipStream_t stream);
+
+/* One fp32 gradient tensor for moon_reduce_grad (Guide, Buffer.reduce_grad;
+ * README, Gradient buffer), split like moon_weight_tensor:
+ *   expert_grads [E, row_elems]     the owners' parameter gradients, updated
+ *   slot_grads   [R, B, row_elems]  every rank's reduce buffer, used slots cleared
+ * row_elems = H*H', a positive multiple of 4; both pointers 16-byte aligned. */
+typedef struct {
+  float* expert_grads;
+  float* slot_grads;
+  int64_t row_elems;
+} moon_grad_tensor;
+
+/* Gradient reduction (Guide, Buffer.reduce_grad): for every tensor and every
+ * expert e held by at least one slot, expert_grads[e] <- expert_grads[e] +
+ * slot_grads[u][j] for each rank u in ascending order whose slot j holds e
+ * (fp32 adds, one after another, seeded with the expert's own gradient);
+ * then every used slot's gradient row is set to +0.0.  Experts no slot holds
+ * and unused slots are not touched.  n_tensors in [1, 8].  Asynchronous on
+ * `stream`; uses context scratch.  A plan whose device status is not OK
+ * writes nothing. */
+moon_status moon_reduce_grad(moon_ctx* ctx, const moon_comm_plan* plan,
+                             const moon_grad_tensor* tensors, int32_t n_tensors,
+                             hipStream_t stream);
+
 const char* moon_status_str(moon_status s);
 
 #ifdef __cplusplus

@@ -22,7 +22,7 @@ def test_header_declares_the_path():
     for n in ("moon_plan", "moon_dispatch", "moon_combine", "moon_prefetch_index",
               "moon_ctx_create", "moon_ctx_destroy", "moon_plan_create", "moon_plan_clone",
               "moon_plan_destroy", "moon_plan_status", "moon_plan_view", "moon_ctx_layout",
-              "moon_status_str"):
+              "moon_status_str", "moon_prefetch_weight", "moon_reduce_grad"):
         assert n in names
 
 
@@ -75,6 +75,8 @@ def test_null_handles_are_rejected(moon):
     assert lib.moon_combine(None, None, None, None, 0, None, None, None) == \
         moon.MOON_ERR_INVALID_ARG
     assert lib.moon_prefetch_index(None, None, None, None) == moon.MOON_ERR_INVALID_ARG
+    assert lib.moon_prefetch_weight(None, None, None, 0, None) == moon.MOON_ERR_INVALID_ARG
+    assert lib.moon_reduce_grad(None, None, None, 0, None) == moon.MOON_ERR_INVALID_ARG
     assert lib.moon_plan_status(None, None) == moon.MOON_ERR_INVALID_ARG
     # destroy is idempotent on NULL
     p = ctypes.c_void_p()
