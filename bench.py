@@ -229,6 +229,81 @@ def measure_weights(moon, ctx, s, stream, iters, hp):
     }
 
 
+def measure_serving(moon, dev, stream, steps, warmup):
+    """The padded serving workload per level: plan (with the tokens_per_expert
+    histogram) -> dispatch -> plain K-sum combine -> prefetch index, timed per
+    call with HIP events on `stream`."""
+    import torch
+    import synth
+    import synth.gpu as sg
+    res = []
+    for level in range(len(synth.SERVING_LEVELS)):
+        wl = synth.serving_workload(level)
+        R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+        ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+        plan = moon.moon_plan_create(ctx)
+        topk = torch.from_numpy(wl["topk"]).to(dev)
+        tpe = torch.from_numpy(wl["tokens_per_expert"]).to(dev)
+        w = torch.from_numpy(wl["w"]).to(dev)
+        hidden = sg.hidden(wl["seed"], R, S, H, dev)
+        for r in range(R):
+            hidden[r, int(wl["n_tok"][r]):] = 0
+        y = sg.y(wl["seed"], R * ctx.NvS, H, dev)
+        out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
+        pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
+        win, wwin = moon.window_tensors(ctx)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            moon.moon_plan(ctx, topk, tpe, plan, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            moon.moon_dispatch(ctx, plan, hidden, w, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+            moon.moon_combine(ctx, plan, y, None, 0, out, None, stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+            moon.moon_prefetch_index(ctx, plan, pidx, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        st = moon.moon_plan_status(plan, stream)
+        if st != moon.MOON_OK:
+            raise RuntimeError(f"serving plan status {moon.moon_status_str(st)}")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for ev in evs:
+            step(ev)
+        torch.cuda.synchronize()
+        t = [sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / steps * 1e3 for i in range(3)]
+        nb = algorithmic_bytes(moon, ctx, plan)
+        nb["combine"] -= 4 * nb["n_route"] * 2  # no weight read, no weight gather
+        real = int(wl["n_tok"].sum())
+        res.append({
+            "level": wl["level_name"], "S": S, "real_tokens": real, "maxvio": round(wl["maxvio"], 2),
+            "ms_per_step": round(ms, 4), "plan_us": round(t[0], 2), "dispatch_us": round(t[1], 2),
+            "combine_us": round(t[2], 2),
+            "dispatch_GBps": round(nb["dispatch"] / (t[1] * 1e-6) / 1e9, 1),
+            "combine_GBps": round(nb["combine"] / (t[2] * 1e-6) / 1e9, 1),
+            "real_tokens_per_s": round(real / (ms * 1e-3)),
+            "capacity_tokens_per_s": round(R * S / (ms * 1e-3)),
+            "dup_rows": nb["n_dup"], "slots_used": nb["slots_used"]})
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
+        del hidden, y, out, win, wwin
+        torch.cuda.empty_cache()
+    return res
+
+
 def source_hash(files):
     h = hashlib.sha256()
     for f in files:
@@ -500,6 +575,9 @@ def main():
     weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
                               FFN_WIDTH[config])
 
+    log("[bench] padded serving workload")
+    serving = measure_serving(moon, dev, stream, max(10, args.steps // 5), 3)
+
     sweep = []
     if not args.no_sweep and config == 2:
         # maxvio sweep on the same shapes: level "0" is this workload's routing,
@@ -558,6 +636,7 @@ def main():
         "dispatch_roofline": dispatch_roofline,
         "ablations": ablations,
         "weights": weights,
+        "serving": serving,
         "cpu_baseline": cpu,
     }
     for s in sets:

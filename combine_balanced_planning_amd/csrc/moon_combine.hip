@@ -30,7 +30,9 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
-constexpr int kUnroll = 2;  // routed slices in flight per wave
+constexpr int kUnroll = 2;  // rows in flight per wave in the prologue fold
+constexpr int kCombineSliceVec = 1;  // 16-byte vectors per lane in a gather slice
+constexpr int kCombineUnroll = 2;    // routed rows loaded before they are summed
 constexpr int kFoldBlocks = 8192;  // persistent grid of the prologue
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -118,20 +120,21 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-template <bool PROLOGUE>
+template <bool PROLOGUE, int SV, int KU>
 __global__ void __launch_bounds__(kThreads)
     k_combine(Dims d, PlanArrays pa, const u32x4* __restrict__ y, const float* __restrict__ wnvs,
               int weighted, const u32x4* __restrict__ fold, u32x4* __restrict__ out,
               float* __restrict__ wsk) {
   if (pa.status[0] != 0) return;
+  constexpr int SW = kWave * SV;  // vectors per slice
   const int lane = threadIdx.x & (kWave - 1);
   const int V = d.H / 8;
-  const int nsl = (V + kWave - 1) / kWave;
+  const int nsl = (V + SW - 1) / SW;
   const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   if (item >= (int64_t)d.R * d.S * nsl) return;
   const int64_t t = item / nsl;
   const int sl = (int)(item - t * nsl);
-  const int j = sl * kWave + lane;  // this lane's vector of the row
+  const int j0 = sl * SW + lane;  // this lane's vectors: j0 + c * kWave
   int gl = 0, dl = 0;
   float wl = 0.0f;
   if (lane < d.K) {
@@ -152,15 +155,17 @@ __global__ void __launch_bounds__(kThreads)
     }
     folded = folded && dl >= 0 && lane < d.K;
   }
-  float acc[8];
+  float acc[SV][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int k0 = 0; k0 < d.K; k0 += kUnroll) {
-    u32x4 buf[kUnroll];
-    float ck[kUnroll];
-    bool use[kUnroll];
+  for (int c = 0; c < SV; ++c)
 #pragma unroll
-    for (int uu = 0; uu < kUnroll; ++uu) {
+    for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
+  for (int k0 = 0; k0 < d.K; k0 += KU) {
+    u32x4 buf[KU][SV];
+    float ck[KU];
+    bool use[KU];
+#pragma unroll
+    for (int uu = 0; uu < KU; ++uu) {
       const int k = min(k0 + uu, d.K - 1);
       const int G = __builtin_amdgcn_readlane(gl, k);
       ck[uu] = weighted ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), k)) : 1.0f;
@@ -173,23 +178,35 @@ __global__ void __launch_bounds__(kThreads)
           ck[uu] = 1.0f;
         }
       }
-      if (j < V && use[uu]) buf[uu] = __builtin_nontemporal_load(src + (int64_t)G * V + j);
-    }
+      const u32x4* row = src + (int64_t)G * V;
 #pragma unroll
-    for (int uu = 0; uu < kUnroll; ++uu) {
-      if (!use[uu]) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q + 0] = acc[2 * q + 0] + ck[uu] * bf16_lo(buf[uu][q]);
-        acc[2 * q + 1] = acc[2 * q + 1] + ck[uu] * bf16_hi(buf[uu][q]);
+      for (int c = 0; c < SV; ++c) {
+        const int j = j0 + c * kWave;
+        if (j < V && use[uu]) buf[uu][c] = __builtin_nontemporal_load(row + j);
       }
     }
-  }
-  if (j < V) {
-    u32x4 v;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
-    __builtin_nontemporal_store(v, out + t * V + j);
+    for (int uu = 0; uu < KU; ++uu) {
+      if (!use[uu]) continue;
+#pragma unroll
+      for (int c = 0; c < SV; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[c][2 * q + 0] = acc[c][2 * q + 0] + ck[uu] * bf16_lo(buf[uu][c][q]);
+          acc[c][2 * q + 1] = acc[c][2 * q + 1] + ck[uu] * bf16_hi(buf[uu][c][q]);
+        }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < SV; ++c) {
+    const int j = j0 + c * kWave;
+    if (j < V) {
+      u32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] = bf16_rne(acc[c][2 * q]) | (bf16_rne(acc[c][2 * q + 1]) << 16);
+      __builtin_nontemporal_store(v, out + t * V + j);
+    }
   }
 }
 
@@ -207,7 +224,8 @@ __global__ void k_prefetch_index(Dims d, PlanArrays pa, int32_t* __restrict__ ou
 hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y,
                           const float* wnvs, bool weighted, uint16_t* fold, uint16_t* out,
                           float* wsk, hipStream_t s) {
-  const int nsl = (d.H / 8 + kWave - 1) / kWave;
+  constexpr int SV = kCombineSliceVec, KU = kCombineUnroll;
+  const int nsl = (d.H / 8 + kWave * SV - 1) / (kWave * SV);
   const int64_t items = (int64_t)d.R * d.S * nsl;
   const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -215,19 +233,20 @@ hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y
   auto* fv = reinterpret_cast<u32x4*>(fold);
   if (fold != nullptr && d.K > 1) {
     // persistent grid over (duplicate group, slice) items, sized like the gather
-    const int64_t fw = (int64_t)d.R * d.S * nsl;
+    const int fnsl = (d.H / 8 + kWave - 1) / kWave;
+    const int64_t fw = (int64_t)d.R * d.S * fnsl;
     const int64_t want = (fw + kWavesPerBlock - 1) / kWavesPerBlock;
     const int fblocks = (int)(want < kFoldBlocks ? (want > 0 ? want : 1) : kFoldBlocks);
     hipLaunchKernelGGL(k_combine_fold, dim3(fblocks), dim3(kThreads), 0, s, d, pa, yv, wnvs,
                        weighted ? 1 : 0, fv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_combine<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, d, pa, yv,
-                       wnvs, weighted ? 1 : 0, fv, reinterpret_cast<u32x4*>(out), wsk);
+    hipLaunchKernelGGL((k_combine<true, SV, KU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, d,
+                       pa, yv, wnvs, weighted ? 1 : 0, fv, reinterpret_cast<u32x4*>(out), wsk);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_combine<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, d, pa, yv,
-                     wnvs, weighted ? 1 : 0, nullptr, reinterpret_cast<u32x4*>(out), wsk);
+  hipLaunchKernelGGL((k_combine<false, SV, KU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, d,
+                     pa, yv, wnvs, weighted ? 1 : 0, nullptr, reinterpret_cast<u32x4*>(out), wsk);
   return hipGetLastError();
 }
 

@@ -14,8 +14,10 @@
 //                       to each primary row of the token; slice 0 also
 //                       scatters the K route weights.  Further items zero the
 //                       padding rows of every (rank, group), eight rows each.
-//   k_dispatch_expand   persistent grid; one wave per duplicate group reads
-//                       the primary row and stores it to each duplicate row.
+//   k_dispatch_expand   persistent grid; a work item is one wave on a 4 KB
+//                       slice of one duplicate group's primary row; the lanes
+//                       also fetch the group's duplicate row offsets, then the
+//                       slice is stored to each duplicate row.
 //
 // All copies move bits; no floating-point arithmetic is done.
 #include "moon_internal.h"
@@ -29,6 +31,8 @@ constexpr int kSliceVec = 2;       // 16-byte vectors per lane in a scatter slic
 constexpr int kZeroRows = 8;       // padding rows per zero-fill item
 constexpr int kScatterBlocks = 8192;
 constexpr int kExpandBlocks = 8192;
+constexpr int kExpandSliceVec = 4;  // 16-byte vectors per lane in an epilogue slice
+constexpr int kExpandUnroll = 1;    // epilogue items a wave has in flight
 
 __global__ void __launch_bounds__(kThreads)
     k_dispatch_scatter(Dims d, PlanArrays pa, const u32x4* __restrict__ hidden,
@@ -88,12 +92,17 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-template <int CH>
+// Work item = (duplicate group, slice of SW = 64*SV vectors).  A wave takes UI
+// items at once: it loads their records, then their primary slices and (one
+// lane per duplicate) their duplicate row offsets, then stores.
+template <int SV, int UI>
 __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays pa,
                                                               u32x4* __restrict__ win) {
   if (pa.status[0] != 0) return;
+  constexpr int SW = kWave * SV;
   const int lane = threadIdx.x & (kWave - 1);
   const int V = d.H / 8;
+  const int nsl = (V + SW - 1) / SW;
   // Groups of all ranks form one list: rank u's groups follow those of ranks < u.
   const int c = lane < d.R ? pa.dup_counts[lane * 2] : 0;
   int incl = c;
@@ -102,42 +111,54 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays
     const int t = __shfl_up(incl, off, kWave);
     if (lane >= off) incl += t;
   }
-  const int total = __shfl(incl, kWave - 1, kWave);
-  const int nwaves = gridDim.x * kWavesPerBlock;
-  for (int gi = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; gi < total; gi += nwaves) {
-    const int u = __popcll(__ballot(lane < d.R && incl <= gi));
-    const int first = __shfl(incl - c, u, kWave);
-    const int32_t* rec = pa.dup_groups + ((int64_t)u * d.NvS + (gi - first)) * 3;
-    const int prow = rec[0], lb = rec[1], m = rec[2];
-    const u32x4* sp = win + ((int64_t)u * d.NvS + prow) * V;
-    const int32_t* lo = pa.dup_loffs + (int64_t)u * d.NvS + lb;
-    for (int c0 = 0; c0 < V; c0 += kWave * CH) {
-      u32x4 buf[CH];
+  const int64_t items = (int64_t)__shfl(incl, kWave - 1, kWave) * nsl;
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t it0 = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; it0 < items;
+       it0 += nwaves * UI) {
+    int64_t base[UI];
+    int prow[UI], m[UI], j0[UI], loff[UI];
 #pragma unroll
-      for (int cc = 0; cc < CH; ++cc) {
-        const int j = c0 + cc * kWave + lane;
-        if (j < V) buf[cc] = sp[j];
+    for (int i = 0; i < UI; ++i) {
+      const int64_t it = it0 + i * nwaves;
+      m[i] = 0;
+      base[i] = 0;
+      prow[i] = 0;
+      j0[i] = 0;
+      loff[i] = 0;
+      if (it < items) {
+        const int gi = (int)(it / nsl), sl = (int)(it - (int64_t)gi * nsl);
+        const int u = __popcll(__ballot(lane < d.R && incl <= gi));
+        const int first = __shfl(incl - c, u, kWave);
+        const int32_t* rec = pa.dup_groups + ((int64_t)u * d.NvS + (gi - first)) * 3;
+        base[i] = (int64_t)u * d.NvS;
+        prow[i] = rec[0];
+        m[i] = rec[2];
+        j0[i] = sl * SW + lane;
+        loff[i] = lane < m[i] ? pa.dup_loffs[base[i] + rec[1] + lane] : 0;
       }
-      for (int i = 0; i < m; ++i) {
-        u32x4* dp = win + ((int64_t)u * d.NvS + lo[i]) * V;
+    }
+    u32x4 buf[UI][SV];
 #pragma unroll
-        for (int cc = 0; cc < CH; ++cc) {
-          const int j = c0 + cc * kWave + lane;
-          if (j < V) __builtin_nontemporal_store(buf[cc], dp + j);
+    for (int i = 0; i < UI; ++i) {
+      const u32x4* sp = win + (base[i] + prow[i]) * V;
+#pragma unroll
+      for (int cc = 0; cc < SV; ++cc) {
+        const int j = j0[i] + cc * kWave;
+        if (m[i] > 0 && j < V) buf[i][cc] = sp[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UI; ++i) {
+      for (int x = 0; x < m[i]; ++x) {
+        u32x4* dp = win + (base[i] + __builtin_amdgcn_readlane(loff[i], x)) * V;
+#pragma unroll
+        for (int cc = 0; cc < SV; ++cc) {
+          const int j = j0[i] + cc * kWave;
+          if (j < V) __builtin_nontemporal_store(buf[i][cc], dp + j);
         }
       }
     }
   }
-}
-
-template <int CH>
-hipError_t launch_expand(const Dims& d, const PlanArrays& pa, uint16_t* win, hipStream_t s) {
-  const int64_t tokens = (int64_t)d.R * d.S;
-  const int64_t want = (tokens + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int blocks = (int)(want < kExpandBlocks ? (want > 0 ? want : 1) : kExpandBlocks);
-  hipLaunchKernelGGL(k_dispatch_expand<CH>, dim3(blocks), dim3(kThreads), 0, s, d, pa,
-                     reinterpret_cast<u32x4*>(win));
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -155,14 +176,16 @@ hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* 
                      wwin, fused ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused || d.K == 1) return e;
-  // Vectors per lane per pass of the epilogue: the smallest count covering a row.
-  const int per_lane = (V + kWave - 1) / kWave;
-  if (per_lane <= 1) return launch_expand<1>(d, pa, win, s);
-  if (per_lane <= 2) return launch_expand<2>(d, pa, win, s);
-  if (per_lane <= 4) return launch_expand<4>(d, pa, win, s);
-  if (per_lane <= 8) return launch_expand<8>(d, pa, win, s);
-  if (per_lane <= 14) return launch_expand<14>(d, pa, win, s);
-  return launch_expand<16>(d, pa, win, s);
+  // The group count is only known on the device; size the persistent grid by
+  // its bound R*S*(K/2) (a token has at most K/2 groups), times the slices.
+  constexpr int SW = kWave * kExpandSliceVec;
+  const int64_t bound = (int64_t)d.R * d.S * (d.K / 2) * ((V + SW - 1) / SW);
+  const int64_t ewant = (bound + kWavesPerBlock * kExpandUnroll - 1) /
+                        (kWavesPerBlock * kExpandUnroll);
+  const int eblocks = (int)(ewant < kExpandBlocks ? (ewant > 0 ? ewant : 1) : kExpandBlocks);
+  hipLaunchKernelGGL((k_dispatch_expand<kExpandSliceVec, kExpandUnroll>), dim3(eblocks),
+                     dim3(kThreads), 0, s, d, pa, reinterpret_cast<u32x4*>(win));
+  return hipGetLastError();
 }
 
 }  // namespace moon

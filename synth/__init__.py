@@ -33,6 +33,7 @@ M64 = (1 << 64) - 1
 GAMMA = 0x9E3779B97F4A7C15
 
 TAG_HIDDEN, TAG_Y, TAG_LOGIT_A, TAG_LOGIT_B, TAG_PERM, TAG_HOME = 1, 2, 3, 4, 5, 6
+TAG_NTOK, TAG_INVALID = 7, 8
 
 
 def _mix64_int(z):
@@ -164,6 +165,18 @@ CONFIGS = {
     5: dict(name="r16-e384-k8-s8192-h7168-dedup", R=16, E=384, K=8, S=8192, H=7168, P=128, B=24,
             dedup_stress=True),
 }
+# Serving workload with capacity padding (the serving integration's buffer
+# pool): per rank a step holds n_r real tokens drawn uniformly from [lo, hi];
+# the buffer capacity S is the smallest power of two >= max_r n_r, clamped to
+# [min_capacity, max_tokens].  Real tokens route like the DSv3-shaped
+# configuration; about one real route slot in `invalid_every` is an invalid
+# id that the engine maps to expert 0 with weight 0; pad tokens have zero
+# hidden rows, all K ids 0 and weights 0.  Combine is the plain K-sum.
+SERVING = dict(name="serving-padded-r8-e256-k8-h7168", R=8, E=256, K=8, H=7168, P=128, B=32,
+               max_tokens=4096, min_capacity=128, invalid_every=64, dedup_stress=False)
+SERVING_LEVELS = [dict(name="decode", lo=48, hi=200), dict(name="prefill", lo=1200, hi=3000)]
+SERVING_CONFIG = 6
+
 # maxvio targets per configuration (level index -> target); None = no bias.
 LEVELS = {1: [None], 2: [None], 3: [None], 4: [0.5, 1.0, 2.0, 4.0], 5: [None, 1.0, 2.0, 4.0, 8.0]}
 
@@ -271,3 +284,45 @@ def hidden_bf16(seed, R, S, H):
 
 def y_bf16(seed, rows, H):
     return bf16_normal(stream_key(seed, TAG_Y), 0, rows * H).reshape(rows, H)
+
+
+def serving_capacity(n_max, min_capacity, max_tokens):
+    """Smallest power of two >= n_max, clamped to [min_capacity, max_tokens]."""
+    if n_max >= max_tokens:
+        return max_tokens
+    cap = 1 << max(n_max - 1, 0).bit_length()
+    return min(max(cap, min_capacity), max_tokens)
+
+
+def serving_workload(level):
+    """The padded serving workload at `level` (index into SERVING_LEVELS): dict
+    with the shapes (S = capacity), n_tok [R], topk [R,S,K], w [R,S,K],
+    tokens_per_expert [R,E] (bincount of the padded ids) and maxvio."""
+    c = dict(SERVING)
+    lv = SERVING_LEVELS[level]
+    seed = seed_of(SERVING_CONFIG, level)
+    R, E, K = c["R"], c["E"], c["K"]
+    span = np.uint64(lv["hi"] - lv["lo"] + 1)
+    n_tok = (lv["lo"] + (words(stream_key(seed, TAG_NTOK), 0, R) % span)).astype(np.int64)
+    S = serving_capacity(int(n_tok.max()), c["min_capacity"], c["max_tokens"])
+    c.update(S=S)
+    topk, w = routing(None, seed, 0.0, cfg=c)
+    invalid = (words(stream_key(seed, TAG_INVALID), 0, R * S * K) %
+               np.uint64(c["invalid_every"]) == 0).reshape(R, S, K)
+    pad = np.arange(S)[None, :] >= n_tok[:, None]
+    invalid |= pad[:, :, None]
+    topk = np.where(invalid, 0, topk).astype(np.int32)
+    w = np.where(invalid, np.float32(0.0), w).astype(np.float32)
+    tpe = np.stack([np.bincount(topk[r].reshape(-1), minlength=E) for r in range(R)])
+    c.update(seed=seed, level=level, level_name=lv["name"], n_tok=n_tok, topk=topk, w=w,
+             tokens_per_expert=tpe.astype(np.int32), maxvio=maxvio(topk, E),
+             config=SERVING_CONFIG)
+    return c
+
+
+def serving_hidden_bf16(wl):
+    """bf16 hidden [R,S,H] of a serving workload: N(0,1) rows, pad rows zero."""
+    h = hidden_bf16(wl["seed"], wl["R"], wl["S"], wl["H"])
+    for r in range(wl["R"]):
+        h[r, wl["n_tok"][r]:] = 0
+    return h

@@ -32,7 +32,7 @@ def say(*a):
 
 
 def run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, dflags=0, weighted=True,
-             label=""):
+             label="", tpe=None):
     """Plan + dispatch + combine on the GPU with full comparisons to the oracle."""
     import torch
     say(f"[case] {label} R={R} E={E} K={K} S={S} H={H} B={B} P={P} dflags={dflags}")
@@ -40,7 +40,7 @@ def run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, dflags=0, weigh
     plan = moon.moon_plan_create(ctx)
     try:
         topk_d = pt.to_dev(topk, dev)
-        moon.moon_plan(ctx, topk_d, None, plan)
+        moon.moon_plan(ctx, topk_d, pt.to_dev(tpe, dev) if tpe is not None else None, plan)
         moon.moon_dispatch(ctx, plan, pt.bf16_to_dev(hidden, dev),
                            pt.to_dev(w, dev) if w is not None else None, flags=dflags)
         win, wwin = moon.window_tensors(ctx)
@@ -54,7 +54,7 @@ def run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, dflags=0, weigh
         assert moon.moon_plan_status(plan) == moon.MOON_OK
         got = pt.gpu_plan_arrays(plan)
 
-        ref = oracle.plan(topk, E, ctx.B, P)
+        ref = oracle.plan(topk, E, ctx.B, P, tpe)
         assert ref.status == oracle.OK and ref.NvS == ctx.NvS
         pt.compare_plan(got, ref)
         pc.check_all(pt.gpu_plan_view(got, ref), topk, dups=R * S <= 4096)
