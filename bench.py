@@ -5,13 +5,16 @@ plan (histogram, balance, layout, placement, duplicate records) -> dispatch
 (scatter + zero-fill + dedup epilogue) -> combine (weighted K-sum + weight
 gather) -> prefetch index.  Inputs are resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3] [--step-only]
 
 Prints one JSON line.  `value` is the dispatch+combine algorithmic HBM bytes
 of a step divided by the measured time of the whole step (plan included), in
-GB/s; the line also carries tokens/s, per-call times (HIP events on the
-stream the kernels run on), a maxvio sweep on the same shapes, the roofline
-of the dominant kernel and the oracle timed on the host as a CPU baseline.
+GB/s; the line also carries tokens/s, per-call times inside the step (HIP
+events on the stream the kernels run on), the roofline of the dominant kernel
+(its duration from back-to-back launches on the timed inputs), a maxvio sweep
+on the same shapes, the dedup ablations, weight prefetch and gradient
+reduction, the padded serving workload and the oracle timed on the host as a
+CPU baseline.  --step-only keeps just the step (the profiler runs use it).
 """
 import argparse
 import hashlib
@@ -100,7 +103,7 @@ def run_steps(moon, ctx, sets, steps, warmup, stream):
         if ev is not None:
             ev[4].record(stream)
 
-    for i in range(warmup):
+    for i in range(max(warmup, len(sets))):  # every input set planned at least once
         step(i)
     torch.cuda.synchronize()
     for s in sets:
@@ -133,19 +136,32 @@ def run_steps(moon, ctx, sets, steps, warmup, stream):
         calls["combine"] += ev[2].elapsed_time(ev[3])
         calls["prefetch_index"] += ev[3].elapsed_time(ev[4])
     calls = {k: v / steps * 1e3 for k, v in calls.items()}  # microseconds
-    return ms_step, wall, calls
+
+    # launch durations: the same calls back to back between two events (no
+    # event markers between launches), on the input sets of the timed steps
+    launch = {
+        "combine": time_call(lambda i=0: moon.moon_combine(
+            ctx, sets[i % len(sets)].plan, sets[i % len(sets)].y, wwin,
+            moon.MOON_COMBINE_WEIGHTED, sets[i % len(sets)].out, sets[i % len(sets)].wsk,
+            stream=stream), steps, stream),
+        "dispatch": time_call(lambda i=0: moon.moon_dispatch(
+            ctx, sets[i % len(sets)].plan, sets[i % len(sets)].hidden, sets[i % len(sets)].w,
+            stream=stream), steps, stream),
+    }
+    return ms_step, wall, calls, launch
 
 
 def time_call(fn, iters, stream):
-    """Average microseconds of `fn` over `iters` back-to-back calls (HIP events on `stream`)."""
+    """Average microseconds of `fn` over `iters` back-to-back calls (HIP events
+    on `stream`); `fn` may take the call index."""
     import torch
     for _ in range(3):
         fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(iters):
-        fn()
+    for i in range(iters):
+        fn(i)
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / iters * 1e3
@@ -158,15 +174,15 @@ def measure_ablations(moon, ctx, s, nb, stream, iters):
     c = ctx.cfg
     row = 2 * c.H
     win, wwin = moon.window_tensors(ctx)
-    t_fused = time_call(lambda: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w,
+    t_fused = time_call(lambda i=0: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w,
                                                    flags=moon.MOON_DISPATCH_FUSED_DUPS,
                                                    stream=stream), iters, stream)
-    t_epi = time_call(lambda: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream),
+    t_epi = time_call(lambda i=0: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream),
                       iters, stream)
     flags = moon.MOON_COMBINE_WEIGHTED | moon.MOON_COMBINE_DUP_PROLOGUE
-    t_pro = time_call(lambda: moon.moon_combine(ctx, s.plan, s.y, wwin, flags, s.out, s.wsk,
+    t_pro = time_call(lambda i=0: moon.moon_combine(ctx, s.plan, s.y, wwin, flags, s.out, s.wsk,
                                                 stream=stream), iters, stream)
-    t_plain = time_call(lambda: moon.moon_combine(ctx, s.plan, s.y, wwin,
+    t_plain = time_call(lambda i=0: moon.moon_combine(ctx, s.plan, s.y, wwin,
                                                   moon.MOON_COMBINE_WEIGHTED, s.out, s.wsk,
                                                   stream=stream), iters, stream)
     # prologue: every group reads its m+1 rows (and weights) and writes one
@@ -208,13 +224,13 @@ def measure_weights(moon, ctx, s, stream, iters, hp):
     w = [sg.fill_bf16(torch.empty((c.E, L), dtype=torch.bfloat16, device="cuda"), key, i * c.E * L)
          for i in range(3)]
     sl = [torch.zeros((c.R, ctx.B, L), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
-    t_pw = time_call(lambda: moon.moon_prefetch_weight(ctx, s.plan, w, sl, stream=stream), iters,
+    t_pw = time_call(lambda i=0: moon.moon_prefetch_weight(ctx, s.plan, w, sl, stream=stream), iters,
                      stream)
     del w, sl
     g = [sg.fill_bf16(torch.empty((c.E, L), dtype=torch.bfloat16, device="cuda"), key).float()
          for _ in range(3)]
     sgr = [torch.zeros((c.R, ctx.B, L), dtype=torch.float32, device="cuda") for _ in range(3)]
-    t_rg = time_call(lambda: moon.moon_reduce_grad(ctx, s.plan, g, sgr, stream=stream), iters,
+    t_rg = time_call(lambda i=0: moon.moon_reduce_grad(ctx, s.plan, g, sgr, stream=stream), iters,
                      stream)
     del g, sgr
     torch.cuda.empty_cache()
@@ -312,29 +328,43 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-# Sources whose change invalidates recorded counter readings: the kernels,
-# their launch configuration and the input generator.
-PMC_SOURCES = ["combine_balanced_planning_amd/csrc/moon_internal.h",
-               "combine_balanced_planning_amd/csrc/moon_api.hip",
-               "combine_balanced_planning_amd/csrc/moon_plan.hip",
-               "combine_balanced_planning_amd/csrc/moon_dispatch.hip",
-               "combine_balanced_planning_amd/csrc/moon_combine.hip",
-               "combine_balanced_planning_amd/csrc/moon_weights.hip",
-               "synth/__init__.py"]
+# Sources whose change invalidates a kernel's recorded counter readings: its
+# own file, the shared header and host code (layout, launch checks) and the
+# input generator.
+PMC_COMMON = ["combine_balanced_planning_amd/csrc/moon_internal.h",
+              "combine_balanced_planning_amd/csrc/moon_api.hip",
+              "synth/__init__.py"]
+PMC_KERNEL_FILES = {"k_plan": "combine_balanced_planning_amd/csrc/moon_plan.hip",
+                    "k_dispatch": "combine_balanced_planning_amd/csrc/moon_dispatch.hip",
+                    "k_combine": "combine_balanced_planning_amd/csrc/moon_combine.hip",
+                    "k_prefetch_index": "combine_balanced_planning_amd/csrc/moon_combine.hip"}
+PMC_SOURCES = PMC_COMMON + sorted(set(PMC_KERNEL_FILES.values()))
+
+
+def kernel_sources(kernel):
+    """Files whose content decides `kernel`'s memory traffic."""
+    base = kernel.split("<", 1)[0]
+    own = [f for p, f in PMC_KERNEL_FILES.items() if base.startswith(p)]
+    return PMC_COMMON + own[:1]
 
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary of `workload`, if it was taken on the current sources (else None)."""
+    summary of `workload`, if its sources are unchanged since (else None)."""
     path = os.path.join(PROFILES, f"pmc_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash(rec.get("sources", [])):
+    hashes = rec.get("source_hashes", {})
+    if any(hashes.get(f) != source_hash([f]) for f in kernel_sources(kernel)):
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k["hbm_bytes_per_launch"]
+    # kernel names carry their template arguments; take the instantiation of
+    # `kernel` with the most launches (the counter runs time the step only)
+    cands = [v for n, v in rec.get("kernels", {}).items() if n.split("<", 1)[0] == kernel]
+    if not cands:
+        return None
+    return max(cands, key=lambda v: v["launches"])["hbm_bytes_per_launch"]
 
 
 def short_kernel_name(name):
@@ -385,7 +415,7 @@ def summarize_pmc(workload, dirs, commands):
     rec = {"workload": workload, "commands": commands,
            "calibration": {"kernel": "torch.add(a, 0, out=b), 1 GiB read + 1 GiB written",
                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
-           "sources": PMC_SOURCES, "source_hash": source_hash(PMC_SOURCES), "kernels": kernels}
+           "source_hashes": {f: source_hash([f]) for f in PMC_SOURCES}, "kernels": kernels}
     with open(os.path.join(PROFILES, f"pmc_{workload}.json"), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -405,23 +435,50 @@ def summarize_pmc(workload, dirs, commands):
     print(json.dumps(rec))
 
 
-def summarize_trace(workload, d, command, bench_line=None):
-    """Write profiles/kernels_<workload>.md from a rocprofv3 --stats csv folder."""
+def _trace_rows(d):
+    """Per-dispatch rows of a rocprofv3 --kernel-trace csv folder:
+    (kernel, grid size in work-items, duration ns)."""
     import csv
     import glob
-    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if not files:
-        raise SystemExit(f"no kernel_stats.csv under {d}")
+        raise SystemExit(f"no kernel_trace.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                grid = 1
+                for ax in ("X", "Y", "Z"):
+                    grid *= int(row.get(f"Grid_Size_{ax}", 1) or 1)
+                rows.append((short_kernel_name(row["Kernel_Name"]), grid,
+                             int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+    return rows
+
+
+def summarize_trace(workload, d, command, bench_line=None):
+    """Write profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace
+    csv folder, one line per (kernel, grid size): the same kernel launched on
+    another workload's shape is a line of its own."""
+    groups = {}
+    for name, grid, ns in _trace_rows(d):
+        groups.setdefault((name, grid), []).append(ns)
+    total = sum(sum(v) for v in groups.values())
     lines = [f"# Kernel trace — workload {workload}", "", "Command (repo root, one MI355X):", "",
              "    " + command, "",
-             "| kernel | calls | total µs | avg µs | min µs | max µs | % of GPU time |",
-             "|---|---|---|---|---|---|---|"]
-    with open(files[0], newline="") as f:
-        for row in csv.DictReader(f):
-            lines.append(f"| {short_kernel_name(row['Name'])} | {row['Calls']} | "
-                         f"{float(row['TotalDurationNs']) / 1e3:.1f} | "
-                         f"{float(row['AverageNs']) / 1e3:.2f} | {float(row['MinNs']) / 1e3:.2f} | "
-                         f"{float(row['MaxNs']) / 1e3:.2f} | {float(row['Percentage']):.1f} |")
+             "One line per kernel and grid size (work-items); durations from the per-dispatch "
+             "kernel trace.", "",
+             "| kernel | grid | calls | total µs | avg µs | min µs | max µs | % of GPU time |",
+             "|---|---|---|---|---|---|---|---|"]
+    omitted = 0
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if sum(v) < 1e-3 * total:
+            omitted += 1
+            continue
+        lines.append(f"| {name} | {grid} | {len(v)} | {sum(v) / 1e3:.1f} | "
+                     f"{sum(v) / len(v) / 1e3:.2f} | {min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} | "
+                     f"{100.0 * sum(v) / total:.1f} |")
+    if omitted:
+        lines.append(f"| ({omitted} more lines, each under 0.1 % of GPU time) | | | | | | | |")
     if bench_line:
         with open(bench_line) as f:
             js = [ln for ln in f if ln.startswith("{")]
@@ -487,6 +544,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[2, 3])
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step only: no ablations, weights, serving workload, maxvio "
+                         "sweep or CPU baseline (the counter runs use this)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="run only a plain 1 GiB elementwise copy (scales HBM counters)")
@@ -543,7 +603,7 @@ def main():
             Inputs(moon, ctx, config, seed + 500, 0.0, dev)]
     torch.cuda.synchronize()
     log("[bench] timing")
-    ms_step, wall, calls = run_steps(moon, ctx, sets, args.steps, args.warmup, stream)
+    ms_step, wall, calls, launch = run_steps(moon, ctx, sets, args.steps, args.warmup, stream)
     nb = algorithmic_bytes(moon, ctx, sets[0].plan)
     nb1 = algorithmic_bytes(moon, ctx, sets[1].plan)
     bytes_dc = 0.5 * (nb["dispatch"] + nb["combine"] + nb1["dispatch"] + nb1["combine"])
@@ -552,34 +612,40 @@ def main():
     dc_gbps = bytes_dc / t_dc / 1e9
 
     # Roofline of the dominant kernel: k_combine, the largest single launch of
-    # the step (one launch per combine call, so the call's HIP-event time is
-    # its launch duration).  Dispatch is two launches (scatter + epilogue);
-    # its call-level figure is reported beside it.
+    # the step (one launch per combine call); its duration is the average of
+    # back-to-back launches on the timed inputs.  Dispatch is two launches
+    # (scatter + epilogue); its call-level figure is reported beside it.
     comb_bytes = 0.5 * (nb["combine"] + nb1["combine"])
     disp_bytes = 0.5 * (nb["dispatch"] + nb1["dispatch"])
-    achieved = comb_bytes / (calls["combine"] * 1e-6) / 1e9
+    achieved = comb_bytes / (launch["combine"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": measured_traffic("k_combine", c["name"]),
                 "kernel": "k_combine", "algorithmic_bytes_per_launch": int(comb_bytes),
-                "avg_launch_us": round(calls["combine"], 2)}
-    disp_gbps = disp_bytes / (calls["dispatch"] * 1e-6) / 1e9
+                "avg_launch_us": round(launch["combine"], 2),
+                "in_step_call_us": round(calls["combine"], 2)}
+    disp_gbps = disp_bytes / (launch["dispatch"] * 1e-6) / 1e9
+    t_sc = measured_traffic("k_dispatch_scatter", c["name"])
+    t_ex = measured_traffic("k_dispatch_expand", c["name"])
     dispatch_roofline = {"kernels": "k_dispatch_scatter + k_dispatch_expand",
                          "achieved": round(disp_gbps, 1), "unit": "GB/s",
                          "frac": round(disp_gbps / PEAK_HBM_GBPS, 4),
+                         "traffic": t_sc + t_ex if t_sc is not None and t_ex is not None else None,
                          "algorithmic_bytes_per_call": int(disp_bytes),
-                         "avg_call_us": round(calls["dispatch"], 2)}
+                         "avg_call_us": round(launch["dispatch"], 2),
+                         "in_step_call_us": round(calls["dispatch"], 2)}
 
-    ablations = measure_ablations(moon, ctx, sets[0], nb, stream, max(10, args.steps // 2))
-    log("[bench] weight prefetch and gradient reduction")
-    weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
-                              FFN_WIDTH[config])
-
-    log("[bench] padded serving workload")
-    serving = measure_serving(moon, dev, stream, max(10, args.steps // 5), 3)
+    ablations = weights = serving = None
+    if not args.step_only:
+        ablations = measure_ablations(moon, ctx, sets[0], nb, stream, max(10, args.steps // 2))
+        log("[bench] weight prefetch and gradient reduction")
+        weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
+                                  FFN_WIDTH[config])
+        log("[bench] padded serving workload")
+        serving = measure_serving(moon, dev, stream, max(10, args.steps // 5), 3)
 
     sweep = []
-    if not args.no_sweep and config == 2:
+    if not args.no_sweep and not args.step_only and config == 2:
         # maxvio sweep on the same shapes: level "0" is this workload's routing,
         # then the skewed levels
         sweep.append({"maxvio": round(sets[0].maxvio, 4), "ms_per_step": round(ms_step, 4),
@@ -589,8 +655,8 @@ def main():
             s4 = [Inputs(moon, ctx, 4, synth.seed_of(4, level), synth.alpha_for(4, level), dev),
                   Inputs(moon, ctx, 4, synth.seed_of(4, level) + 500,
                          synth.alpha_for(4, level), dev)]
-            ms4, _, calls4 = run_steps(moon, ctx, s4, max(10, args.steps // 2), args.warmup,
-                                       stream)
+            ms4, _, calls4, _ = run_steps(moon, ctx, s4, max(10, args.steps // 2), args.warmup,
+                                          stream)
             b4 = [algorithmic_bytes(moon, ctx, s.plan) for s in s4]
             by4 = 0.5 * sum(b["dispatch"] + b["combine"] for b in b4)
             sweep.append({"maxvio": round(s4[0].maxvio, 4), "target": target,
@@ -608,7 +674,7 @@ def main():
         flat = None
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.step_only:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(config, seed, args.cpu_budget)
 
