@@ -203,6 +203,11 @@ def measure_ablations(moon, ctx, s, nb, stream, iters):
     }
 
 
+# maxvio sweeps: workload -> (configuration of the skewed levels, levels);
+# r8-e64-k6 sweeps the skewed configuration of its shapes, the large
+# R=16 configuration its own levels 1.. (level 0 is the timed base run).
+SWEEPS = {2: (4, [0, 1, 2, 3]), 5: (5, [1, 2, 3, 4])}
+
 # Expert FFN intermediate width H' per workload: DeepSeek-V3's expert width for
 # the DSv3-shaped workload; H/2 (a reading: the pages give none) for r8-e64-k6.
 FFN_WIDTH = {2: 1024, 3: 2048}
@@ -541,7 +546,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 5])
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
@@ -638,23 +643,27 @@ def main():
     ablations = weights = serving = None
     if not args.step_only:
         ablations = measure_ablations(moon, ctx, sets[0], nb, stream, max(10, args.steps // 2))
-        log("[bench] weight prefetch and gradient reduction")
-        weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
-                                  FFN_WIDTH[config])
-        log("[bench] padded serving workload")
-        serving = measure_serving(moon, dev, stream, max(10, args.steps // 5), 3)
+        if config in FFN_WIDTH:
+            log("[bench] weight prefetch and gradient reduction")
+            weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
+                                      FFN_WIDTH[config])
+        if config == 2:
+            log("[bench] padded serving workload")
+            serving = measure_serving(moon, dev, stream, max(10, args.steps // 5), 3)
 
     sweep = []
-    if not args.no_sweep and not args.step_only and config == 2:
+    if not args.no_sweep and not args.step_only and config in SWEEPS:
         # maxvio sweep on the same shapes: level "0" is this workload's routing,
         # then the skewed levels
         sweep.append({"maxvio": round(sets[0].maxvio, 4), "ms_per_step": round(ms_step, 4),
                       "GBps": round(value, 1), "tokens_per_s": round(R * S / (ms_step * 1e-3))})
-        for level, target in enumerate(synth.LEVELS[4]):
+        sc, levels = SWEEPS[config]
+        for level in levels:
+            target = synth.LEVELS[sc][level]
             log(f"[bench] maxvio level {target}")
-            s4 = [Inputs(moon, ctx, 4, synth.seed_of(4, level), synth.alpha_for(4, level), dev),
-                  Inputs(moon, ctx, 4, synth.seed_of(4, level) + 500,
-                         synth.alpha_for(4, level), dev)]
+            s4 = [Inputs(moon, ctx, sc, synth.seed_of(sc, level), synth.alpha_for(sc, level), dev),
+                  Inputs(moon, ctx, sc, synth.seed_of(sc, level) + 500,
+                         synth.alpha_for(sc, level), dev)]
             ms4, _, calls4, _ = run_steps(moon, ctx, s4, max(10, args.steps // 2), args.warmup,
                                           stream)
             b4 = [algorithmic_bytes(moon, ctx, s.plan) for s in s4]

@@ -294,16 +294,21 @@ def serving_capacity(n_max, min_capacity, max_tokens):
     return min(max(cap, min_capacity), max_tokens)
 
 
-def serving_workload(level):
+def serving_workload(level, n_tok=None):
     """The padded serving workload at `level` (index into SERVING_LEVELS): dict
     with the shapes (S = capacity), n_tok [R], topk [R,S,K], w [R,S,K],
-    tokens_per_expert [R,E] (bincount of the padded ids) and maxvio."""
+    tokens_per_expert [R,E] (bincount of the padded ids) and maxvio.
+    `n_tok` overrides the drawn per-rank real token counts."""
     c = dict(SERVING)
     lv = SERVING_LEVELS[level]
     seed = seed_of(SERVING_CONFIG, level)
     R, E, K = c["R"], c["E"], c["K"]
     span = np.uint64(lv["hi"] - lv["lo"] + 1)
-    n_tok = (lv["lo"] + (words(stream_key(seed, TAG_NTOK), 0, R) % span)).astype(np.int64)
+    if n_tok is None:
+        n_tok = (lv["lo"] + (words(stream_key(seed, TAG_NTOK), 0, R) % span)).astype(np.int64)
+    else:
+        n_tok = np.asarray(n_tok, np.int64)
+        assert n_tok.shape == (R,) and (n_tok >= 0).all()
     S = serving_capacity(int(n_tok.max()), c["min_capacity"], c["max_tokens"])
     c.update(S=S)
     topk, w = routing(None, seed, 0.0, cfg=c)

@@ -49,6 +49,20 @@ def test_serving_full_parity_narrow_rows(env, level):
              label=f"serving-{wl['level_name']}-narrow", tpe=wl["tokens_per_expert"])
 
 
+def test_serving_empty_and_full_ranks(env):
+    """Ranks with no real tokens next to ranks filled to capacity."""
+    moon, dev = env
+    wl = dict(synth.serving_workload(0, n_tok=[0, 256, 100, 0, 37, 256, 1, 200]))
+    wl["H"] = 256
+    R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+    hidden = synth.serving_hidden_bf16(wl)
+    y = synth.y_bf16(wl["seed"], R * oracle.nvs(R, E, K, S, B, P), H)
+    for weighted in (False, True):
+        run_full(moon, dev, wl["topk"], wl["w"], hidden, y, R, E, K, S, H, B, P,
+                 weighted=weighted, label=f"serving-empty-ranks-w{int(weighted)}",
+                 tpe=wl["tokens_per_expert"])
+
+
 def _gpu_inputs(moon, dev, wl, ctx):
     import torch
 

@@ -123,3 +123,21 @@ def test_unweighted_round_trip_zeroes_pad_tokens():
     pad = np.arange(wl["S"])[None, :] >= wl["n_tok"][:, None]
     assert (out[pad] == 0).all()
     assert (wsk.view(np.uint32) == wl["w"].view(np.uint32)).all()
+
+
+def test_empty_and_full_ranks():
+    """One rank with no real tokens (its whole capacity is padding, all on
+    expert 0) and one filled to capacity: still a valid, balanced plan, and
+    the empty rank's outputs are all zero."""
+    n = [0, 256, 100, 0, 37, 256, 1, 200]
+    wl = dict(synth.serving_workload(0, n_tok=n))
+    assert wl["S"] == 256
+    assert (wl["topk"][0] == 0).all() and (wl["topk"][3] == 0).all()
+    wl["H"] = NARROW_H
+    pl = _plan(wl)
+    pc.check_all(pc.PlanView.of(pl), wl["topk"])
+    hidden = synth.serving_hidden_bf16(wl)
+    win, _ = oracle.dispatch(pl, hidden, None)
+    out, _, _ = oracle.combine(pl, win, None, weighted=False)
+    assert (out[0] == 0).all() and (out[3] == 0).all()
+    assert (out == _bits(wl["K"] * _f32(hidden))).all()
