@@ -533,8 +533,16 @@ def cpu_baseline(config, seed, budget_s=12.0):
         if time.perf_counter() - t_start >= budget_s:
             break
     total = t_plan + t_disp + t_comb
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": round(bytes_dc * n / total / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": model, "host_cores_available": avail,
             "sample": f"full workload (config {config}, seed {seed}) x {n}: plan "
                       f"{t_plan / n * 1e3:.1f} ms, dispatch {t_disp / n * 1e3:.1f} ms, combine "
                       f"{t_comb / n * 1e3:.1f} ms per step on 1 host core; "
