@@ -125,7 +125,6 @@ __global__ void __launch_bounds__(kThreads)
     k_combine(Dims d, PlanArrays pa, const u32x4* __restrict__ y, const float* __restrict__ wnvs,
               int weighted, const u32x4* __restrict__ fold, u32x4* __restrict__ out,
               float* __restrict__ wsk) {
-  if (pa.status[0] != 0) return;
   constexpr int SW = kWave * SV;  // vectors per slice
   const int lane = threadIdx.x & (kWave - 1);
   const int V = d.H / 8;
@@ -137,8 +136,11 @@ __global__ void __launch_bounds__(kThreads)
   const int j0 = sl * SW + lane;  // this lane's vectors: j0 + c * kWave
   int gl = 0, dl = 0;
   float wl = 0.0f;
+  // The dst entries are read before the plan's status is checked, so the two
+  // loads overlap; nothing read before the check is used unless it is zero.
+  if (lane < d.K) dl = pa.dst[t * d.K + lane];
+  if (pa.status[0] != 0) return;
   if (lane < d.K) {
-    dl = pa.dst[t * d.K + lane];
     gl = (int)dst_global_row(dl);
     if (wnvs != nullptr) wl = wnvs[gl];
     if (wsk != nullptr && sl == 0) wsk[t * d.K + lane] = wl;
@@ -213,8 +215,8 @@ __global__ void __launch_bounds__(kThreads)
 __global__ void k_prefetch_index(Dims d, PlanArrays pa, int32_t* __restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= d.R * d.B) return;
-  const bool ok = pa.status[0] == 0;
-  const int e = ok ? pa.etc[i] : -1;
+  const int ei = pa.etc[i];  // loaded alongside the status word
+  const int e = pa.status[0] == 0 ? ei : -1;
   out[i * 2 + 0] = e >= 0 ? e / d.Eg : -1;
   out[i * 2 + 1] = e >= 0 ? e % d.Eg : -1;
 }

@@ -38,7 +38,9 @@ __global__ void __launch_bounds__(kThreads)
     k_dispatch_scatter(Dims d, PlanArrays pa, const u32x4* __restrict__ hidden,
                        const float* __restrict__ w, u32x4* __restrict__ win,
                        float* __restrict__ wwin, int fused) {
-  if (pa.status[0] != 0) return;
+  // The plan's status is checked before the first store of each work item;
+  // the item's loads do not depend on it, so they overlap with its load.
+  const int status = pa.status[0];
   const int lane = threadIdx.x & (kWave - 1);
   const int V = d.H / 8;
   const int nsl = (V + kWave * kSliceVec - 1) / (kWave * kSliceVec);
@@ -52,10 +54,10 @@ __global__ void __launch_bounds__(kThreads)
       const int64_t t = it / nsl;
       const int sl = (int)(it - t * nsl);
       int dl = 0;
-      if (lane < d.K) {
-        dl = pa.dst[t * d.K + lane];
-        if (w != nullptr && sl == 0) wwin[dst_global_row(dl)] = w[t * d.K + lane];
-      }
+      float wk = 0.0f;
+      const bool wlane = lane < d.K && w != nullptr && sl == 0;
+      if (lane < d.K) dl = pa.dst[t * d.K + lane];
+      if (wlane) wk = w[t * d.K + lane];
       const int c0 = sl * kWave * kSliceVec;
       const u32x4* src = hidden + t * V;
       u32x4 buf[kSliceVec];
@@ -64,6 +66,8 @@ __global__ void __launch_bounds__(kThreads)
         const int j = c0 + c * kWave + lane;
         if (j < V) buf[c] = src[j];
       }
+      if (status != 0) return;
+      if (wlane) wwin[dst_global_row(dl)] = wk;
       for (int k = 0; k < d.K; ++k) {
         const int dk = __builtin_amdgcn_readlane(dl, k);
         if (dk < 0 && !fused) continue;  // duplicate: written by the epilogue
@@ -75,6 +79,7 @@ __global__ void __launch_bounds__(kThreads)
         }
       }
     } else {
+      if (status != 0) return;
       // Zero-fill: rows [a + 8*blk, ..) of one (rank, group) padding range.
       const int64_t z = it - tok_items;
       const int grp = (int)(z / zpg), blk = (int)(z - (int64_t)grp * zpg);
@@ -98,13 +103,14 @@ __global__ void __launch_bounds__(kThreads)
 template <int SV, int UI>
 __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays pa,
                                                               u32x4* __restrict__ win) {
-  if (pa.status[0] != 0) return;
   constexpr int SW = kWave * SV;
   const int lane = threadIdx.x & (kWave - 1);
   const int V = d.H / 8;
   const int nsl = (V + SW - 1) / SW;
   // Groups of all ranks form one list: rank u's groups follow those of ranks < u.
+  // (The counts are loaded alongside the plan's status word.)
   const int c = lane < d.R ? pa.dup_counts[lane * 2] : 0;
+  if (pa.status[0] != 0) return;
   int incl = c;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
