@@ -582,8 +582,9 @@ def main():
             summarize_trace(name, args.summarize_trace, " ".join(args.commands), args.bench_log)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU path is "
-              "not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library emulates "
+              "the R expert-parallel ranks as windows of one GPU's memory and has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
