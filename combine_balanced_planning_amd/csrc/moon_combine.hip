@@ -28,11 +28,13 @@
 namespace moon {
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 16;  // one workgroup = 16 waves (chosen by a sweep of 4, 8, 16)
 constexpr int kThreads = kWavesPerBlock * kWave;
 constexpr int kUnroll = 2;  // rows in flight per wave in the prologue fold
 constexpr int kCombineSliceVec = 1;  // 16-byte vectors per lane in a gather slice
 constexpr int kCombineUnroll = 2;    // routed rows loaded before they are summed
+constexpr bool kCombineNtLoad = true;   // routed rows are read once: non-temporal loads
+constexpr bool kCombineNtStore = true;  // outputs are not read back here: non-temporal stores
 constexpr int kFoldBlocks = 8192;  // persistent grid of the prologue
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -184,7 +186,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int c = 0; c < SV; ++c) {
         const int j = j0 + c * kWave;
-        if (j < V && use[uu]) buf[uu][c] = __builtin_nontemporal_load(row + j);
+        if (j < V && use[uu])
+          buf[uu][c] = kCombineNtLoad ? __builtin_nontemporal_load(row + j) : row[j];
       }
     }
 #pragma unroll
@@ -207,7 +210,8 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         v[q] = bf16_rne(acc[c][2 * q]) | (bf16_rne(acc[c][2 * q + 1]) << 16);
-      __builtin_nontemporal_store(v, out + t * V + j);
+      if (kCombineNtStore) __builtin_nontemporal_store(v, out + t * V + j);
+      else out[t * V + j] = v;
     }
   }
 }

@@ -29,8 +29,8 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
 constexpr int kSliceVec = 2;       // 16-byte vectors per lane in a scatter slice
 constexpr int kZeroRows = 8;       // padding rows per zero-fill item
-constexpr int kScatterBlocks = 8192;
-constexpr int kExpandBlocks = 8192;
+constexpr int kScatterBlocks = 32768;  // persistent grids (a sweep of 2048, 8192, 32768)
+constexpr int kExpandBlocks = 32768;
 constexpr int kExpandSliceVec = 4;  // 16-byte vectors per lane in an epilogue slice
 constexpr int kExpandUnroll = 1;    // epilogue items a wave has in flight
 
