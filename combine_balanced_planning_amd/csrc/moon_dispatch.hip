@@ -11,7 +11,9 @@
 //   k_dispatch_scatter  persistent grid; a work item is one wave on a 2 KB
 //                       slice (128 vectors) of one token's row, read once
 //                       with plain loads and stored with non-temporal stores
-//                       to each primary row of the token; slice 0 also
+//                       to each primary row of the token (cached stores for
+//                       primaries the epilogue re-reads, when all such rows
+//                       fit in a budget of the last-level cache); slice 0 also
 //                       scatters the K route weights.  Further items zero the
 //                       padding rows of every (rank, group), eight rows each.
 //   k_dispatch_expand   persistent grid; a work item is one wave on a 4 KB
@@ -31,13 +33,16 @@ constexpr int kSliceVec = 2;       // 16-byte vectors per lane in a scatter slic
 constexpr int kZeroRows = 8;       // padding rows per zero-fill item
 constexpr int kScatterBlocks = 32768;  // persistent grids (a sweep of 2048, 8192, 32768)
 constexpr int kExpandBlocks = 32768;
+// Half of the 256 MB last-level cache (MI355X): the largest bound on the
+// primary rows the epilogue re-reads for which the scatter caches them.
+constexpr int64_t kKeepBudgetBytes = 128ll << 20;
 constexpr int kExpandSliceVec = 4;  // 16-byte vectors per lane in an epilogue slice
 constexpr int kExpandUnroll = 1;    // epilogue items a wave has in flight
 
 __global__ void __launch_bounds__(kThreads)
     k_dispatch_scatter(Dims d, PlanArrays pa, const u32x4* __restrict__ hidden,
                        const float* __restrict__ w, u32x4* __restrict__ win,
-                       float* __restrict__ wwin, int fused) {
+                       float* __restrict__ wwin, int fused, int keep_dup_primaries) {
   // The plan's status is checked before the first store of each work item;
   // the item's loads do not depend on it, so they overlap with its load.
   const int status = pa.status[0];
@@ -68,14 +73,36 @@ __global__ void __launch_bounds__(kThreads)
       }
       if (status != 0) return;
       if (wlane) wwin[dst_global_row(dl)] = wk;
+      // Lanes k whose primary row the epilogue will read back (a later route
+      // of the token goes to the same rank): stored through the caches when
+      // the host judged that such rows fit in the last-level cache.
+      uint64_t keep = 0;
+      if (keep_dup_primaries) {
+        const int64_t uk = dst_global_row(dl) / d.NvS;
+        for (int k = 1; k < d.K; ++k) {
+          const int dk = __builtin_amdgcn_readlane(dl, k);
+          if (dk < 0) {
+            const int64_t ud = dst_global_row(dk) / d.NvS;
+            keep |= __ballot(lane < k && dl >= 0 && uk == ud);
+          }
+        }
+      }
       for (int k = 0; k < d.K; ++k) {
         const int dk = __builtin_amdgcn_readlane(dl, k);
         if (dk < 0 && !fused) continue;  // duplicate: written by the epilogue
         u32x4* dp = win + dst_global_row(dk) * V;
+        if ((keep >> k) & 1) {
 #pragma unroll
-        for (int c = 0; c < kSliceVec; ++c) {
-          const int j = c0 + c * kWave + lane;
-          if (j < V) __builtin_nontemporal_store(buf[c], dp + j);
+          for (int c = 0; c < kSliceVec; ++c) {
+            const int j = c0 + c * kWave + lane;
+            if (j < V) dp[j] = buf[c];
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < kSliceVec; ++c) {
+            const int j = c0 + c * kWave + lane;
+            if (j < V) __builtin_nontemporal_store(buf[c], dp + j);
+          }
         }
       }
     } else {
@@ -177,9 +204,13 @@ hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* 
   const int64_t items = (int64_t)d.R * d.S * nsl + (int64_t)d.R * d.EB * zpg;
   const int64_t want = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   const int blocks = (int)(want < kScatterBlocks ? (want > 0 ? want : 1) : kScatterBlocks);
+  // The epilogue re-reads at most one primary row per token; when all of
+  // them fit in a budget of the last-level cache, the scatter stores those
+  // rows through the caches so the epilogue can find them there.
+  const int keep = !fused && d.K > 1 && (int64_t)d.R * d.S * d.H * 2 <= kKeepBudgetBytes;
   hipLaunchKernelGGL(k_dispatch_scatter, dim3(blocks), dim3(kThreads), 0, s, d, pa,
                      reinterpret_cast<const u32x4*>(hidden), w, reinterpret_cast<u32x4*>(win),
-                     wwin, fused ? 1 : 0);
+                     wwin, fused ? 1 : 0, keep);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused || d.K == 1) return e;
   // The group count is only known on the device; size the persistent grid by
