@@ -325,11 +325,22 @@ def measure_serving(moon, dev, stream, steps, warmup):
     return res
 
 
+def _code_only(text, path):
+    """Source text without comments and blank space (C/C++/HIP and Python), so
+    that editing a comment does not invalidate recorded counter readings."""
+    if path.endswith(".py"):
+        text = re.sub(r"(?m)#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", " ", text).strip()
+
+
 def source_hash(files):
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read(), f).encode())
     return h.hexdigest()[:16]
 
 

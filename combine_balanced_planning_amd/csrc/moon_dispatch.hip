@@ -33,8 +33,8 @@ constexpr int kSliceVec = 2;       // 16-byte vectors per lane in a scatter slic
 constexpr int kZeroRows = 8;       // padding rows per zero-fill item
 constexpr int kScatterBlocks = 32768;  // persistent grids (a sweep of 2048, 8192, 32768)
 constexpr int kExpandBlocks = 32768;
-// Half of the 256 MB last-level cache (MI355X): the largest bound on the
-// primary rows the epilogue re-reads for which the scatter caches them.
+// Half of the 256 MB last-level cache (MI355X): the largest token-row size
+// R*S*2H of a call for which the scatter caches the re-read primaries.
 constexpr int64_t kKeepBudgetBytes = 128ll << 20;
 constexpr int kExpandSliceVec = 4;  // 16-byte vectors per lane in an epilogue slice
 constexpr int kExpandUnroll = 1;    // epilogue items a wave has in flight
@@ -204,9 +204,10 @@ hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* 
   const int64_t items = (int64_t)d.R * d.S * nsl + (int64_t)d.R * d.EB * zpg;
   const int64_t want = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   const int blocks = (int)(want < kScatterBlocks ? (want > 0 ? want : 1) : kScatterBlocks);
-  // The epilogue re-reads at most one primary row per token; when all of
-  // them fit in a budget of the last-level cache, the scatter stores those
-  // rows through the caches so the epilogue can find them there.
+  // The epilogue re-reads one primary row per duplicate group (about 1.3
+  // per token on uniform routing).  When the call's token rows fit a budget
+  // of the last-level cache, the scatter stores those primaries through the
+  // caches so the epilogue can find them there.
   const int keep = !fused && d.K > 1 && (int64_t)d.R * d.S * d.H * 2 <= kKeepBudgetBytes;
   hipLaunchKernelGGL(k_dispatch_scatter, dim3(blocks), dim3(kThreads), 0, s, d, pa,
                      reinterpret_cast<const u32x4*>(hidden), w, reinterpret_cast<u32x4*>(win),
