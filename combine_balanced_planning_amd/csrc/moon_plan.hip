@@ -6,7 +6,7 @@
 //  and How to set B: each rank ends with S*K routes, the excess going to
 //  redundant-expert slots whose experts all come from one remote home rank.)
 //
-// Three launches on the caller's stream.  Tiles of about 512 routes (more
+// Three launches on the caller's stream.  Tiles of about 768 routes (more
 // when that would give more tiles than compute units) never span two source
 // ranks; a tile is one
 // workgroup of 16 waves; wave w owns a contiguous token range of its tile and
