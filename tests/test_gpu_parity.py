@@ -297,3 +297,27 @@ def test_plan_mismatch_is_rejected(env):
         moon.moon_plan_destroy(p)
         moon.moon_ctx_destroy(c1)
         moon.moon_ctx_destroy(c2)
+
+
+@pytest.mark.parametrize("name", ["alias_worked_example.json", "alias_served_order.json"])
+def test_hand_worked_examples(env, name):
+    """The hand-worked balance examples (tests/golden) through the GPU planner:
+    slots and group sizes as worked out on paper, everything else as the oracle."""
+    import json
+    import os
+    moon, dev = env
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        g = json.load(f)
+    R, E, B, K = g["R"], g["E"], g["B"], 2
+    S, P, H = g["C"] // K, 4, 64
+    routes = np.repeat(np.arange(E), g["T"]).astype(np.int32)
+    topk = routes[np.random.default_rng(9).permutation(routes.shape[0])].reshape(R, S, K)
+    rng = np.random.default_rng(10)
+    w = rng.random((R, S, K)).astype(np.float32)
+    hidden = synth.bf16_normal(synth.stream_key(77, synth.TAG_HIDDEN), 0, R * S * H).reshape(R, S, H)
+    nvs = oracle.nvs(R, E, K, S, B, P)
+    y = synth.bf16_normal(synth.stream_key(77, synth.TAG_Y), 0, R * nvs * H).reshape(R * nvs, H)
+    ref, got = run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, label=name)
+    assert got["experts_to_copy"].tolist() == g["experts_to_copy"]
+    start, n, end = pc.group_table(pt.gpu_plan_view(got, ref))
+    assert n.tolist() == g["n"]

@@ -49,6 +49,17 @@ MUTANTS = {
     "reduce_grad_keeps_slots": ("        if (etc[u * B + j] >= 0)\n          std::fill(",
                                 "        if (etc[u * B + j] >= 1 << 30)\n          std::fill("),
     "reduce_grad_overwrites_seed": ("g[x] = g[x] + sg[x];", "g[x] = sg[x];"),
+    "segments_in_rank_order": ("  for (int u : served) {\n    int o = donor[u];",
+                               "  for (int u = 0; u < R; ++u) {\n    int o = donor[u];\n"
+                               "    if (o < 0) continue;"),
+    "cu_seqlens_exclusive": ("cu[ug] = (int32_t)acc;", "cu[ug] = (int32_t)start[ug];"),
+    "primary_is_last_route": ("for (int k2 = 0; k2 < k; ++k2)", "for (int k2 = k + 1; k2 < K; ++k2)"),
+    "expert_id_E_accepted": ("if (e < 0 || e >= E) return ST_BAD_EXPERT;",
+                             "if (e < 0 || e > E) return ST_BAD_EXPERT;"),
+    "padding_weights_kept": ("if (w != nullptr) wwin[G] = 0.0f;", "(void)w;"),
+    "gathered_weight_of_first_route": ("    if (wsk != nullptr) wsk[k] = wk;",
+                                       "    if (wsk != nullptr) wsk[k] = wat(decode_row(d[0]));"),
+    "capacity_without_slot_padding": ("(Eg + B) * (int64_t)(P - 1)", "Eg * (int64_t)(P - 1)"),
 }
 
 PIN_TESTS = ["tests/test_oracle_plan.py", "tests/test_oracle_data.py", "tests/test_oracle_weights.py"]

@@ -141,13 +141,21 @@ def test_alias_rejects_bad_totals():
     assert oracle.alias(4, [9, -1])[0] == oracle.INVALID
 
 
-def _worked():
-    with open(os.path.join(GOLDEN, "alias_worked_example.json")) as f:
+# Hand-worked balance examples: the first shows why the fill is an alias
+# construction (a plain spill would exceed E/R slots), the second fixes the
+# order in which a donor's receivers cut its stream (the order served).
+GOLDEN_FILES = ["alias_worked_example.json", "alias_served_order.json"]
+
+
+def _worked(name="alias_worked_example.json"):
+    with open(os.path.join(GOLDEN, name)) as f:
         return json.load(f)
 
 
-def test_alias_worked_example():
-    g = _worked()
+@pytest.mark.parametrize("name", GOLDEN_FILES)
+def test_alias_worked_example(name):
+    g = _worked(name)
+    assert sum(g["L"]) == g["R"] * g["C"]
     st, keep, donor, take = oracle.alias(g["C"], g["L"])
     assert st == 0
     assert keep.tolist() == g["keep"]
@@ -155,10 +163,13 @@ def test_alias_worked_example():
     assert take.tolist() == g["take"]
 
 
-def test_plan_worked_example():
-    g = _worked()
+@pytest.mark.parametrize("name", GOLDEN_FILES)
+def test_plan_worked_example(name):
+    g = _worked(name)
     R, E, B = g["R"], g["E"], g["B"]
-    K, S, P = 2, 50, 8
+    K = 2
+    S = g["C"] // K
+    P = 8 if name == GOLDEN_FILES[0] else 2
     assert K * S == g["C"]
     routes = np.repeat(np.arange(E), g["T"]).astype(np.int32)
     routes = routes[np.random.default_rng(5).permutation(routes.shape[0])]
