@@ -167,6 +167,21 @@ def time_call(fn, iters, stream):
     return e0.elapsed_time(e1) / iters * 1e3
 
 
+def measure_copy(stream, nbytes=1 << 30, iters=20):
+    """A plain device-to-device copy of `nbytes` (torch's copy kernel) on the
+    same GPU: read + write bytes per second, the practical ceiling the HBM
+    figures are set against beside the published peak."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    t = time_call(lambda i=0: b.copy_(a), iters, stream)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_per_copy": 2 * nbytes, "us": round(t, 2),
+            "GBps": round(2 * nbytes / (t * 1e-6) / 1e9, 1)}
+
+
 def measure_ablations(moon, ctx, s, nb, stream, iters):
     """The two one-GPU variants of the pages' deduplication on the same input:
     dispatch writing duplicates from registers (no epilogue re-read) and combine
@@ -660,8 +675,11 @@ def main():
                          "avg_call_us": round(launch["dispatch"], 2),
                          "in_step_call_us": round(calls["dispatch"], 2)}
 
-    ablations = weights = serving = None
+    ablations = weights = serving = copy = None
     if not args.step_only:
+        copy = measure_copy(stream)
+        roofline["frac_of_measured_copy"] = round(achieved / copy["GBps"], 4)
+        dispatch_roofline["frac_of_measured_copy"] = round(disp_gbps / copy["GBps"], 4)
         ablations = measure_ablations(moon, ctx, sets[0], nb, stream, max(10, args.steps // 2))
         if config in FFN_WIDTH:
             log("[bench] weight prefetch and gradient reduction")
@@ -730,6 +748,7 @@ def main():
         "roofline": roofline,
         "dispatch_roofline": dispatch_roofline,
         "ablations": ablations,
+        "plain_copy": copy,
         "weights": weights,
         "serving": serving,
         "cpu_baseline": cpu,
