@@ -168,9 +168,9 @@ def time_call(fn, iters, stream):
 
 
 def measure_copy(stream, nbytes=1 << 30, iters=20):
-    """A plain device-to-device copy of `nbytes` (torch's copy kernel) on the
-    same GPU: read + write bytes per second, the practical ceiling the HBM
-    figures are set against beside the published peak."""
+    """The runtime's plain device-to-device copy of `nbytes` (torch's copy_ of
+    a contiguous tensor, a hipMemcpyAsync) on the same GPU: read + write bytes
+    per second, reported beside the published peak as context."""
     import torch
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
@@ -178,7 +178,8 @@ def measure_copy(stream, nbytes=1 << 30, iters=20):
     t = time_call(lambda i=0: b.copy_(a), iters, stream)
     del a, b
     torch.cuda.empty_cache()
-    return {"bytes_per_copy": 2 * nbytes, "us": round(t, 2),
+    return {"what": "hipMemcpyAsync device-to-device (torch copy_)", "bytes_per_copy": 2 * nbytes,
+            "us": round(t, 2),
             "GBps": round(2 * nbytes / (t * 1e-6) / 1e9, 1)}
 
 
