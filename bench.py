@@ -256,11 +256,14 @@ def measure_weights(moon, ctx, s, stream, iters, hp):
     del g, sgr
     torch.cuda.empty_cache()
     pw_bytes = 3 * n_used * L * 2 * 2          # read the expert row, write the slot
+    pw_min = 3 * (n_held + n_used) * L * 2     # each held expert read once, each slot written
     rg_bytes = 3 * (n_held + n_used) * L * 4 * 2  # expert row read+write; slot read+clear
     return {
         "ffn_width": hp, "tensors": 3, "slots_used": n_used, "experts_held": n_held,
         "prefetch_weight_us": round(t_pw, 2), "prefetch_weight_bytes": pw_bytes,
         "prefetch_weight_GBps": round(pw_bytes / (t_pw * 1e-6) / 1e9, 1),
+        "prefetch_weight_min_bytes": pw_min,
+        "prefetch_weight_min_GBps": round(pw_min / (t_pw * 1e-6) / 1e9, 1),
         "reduce_grad_us": round(t_rg, 2), "reduce_grad_bytes": rg_bytes,
         "reduce_grad_GBps": round(rg_bytes / (t_rg * 1e-6) / 1e9, 1),
     }

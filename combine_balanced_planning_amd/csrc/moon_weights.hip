@@ -14,13 +14,14 @@
 // of all ranks are one [R, B, row] array, so the remote transfer becomes an
 // HBM copy of whole expert rows.  Bound: HBM bandwidth.
 //
-//   k_slot_index    one workgroup: the list of used slots (ascending), and
+//   k_slot_index    (gradient reduction) one workgroup: the list of used
+//                   slots (ascending), and
 //                   for every expert held by a slot, its slot on each rank
 //                   (experts ascending).  Both lists go to context scratch.
-//   k_prefetch_copy persistent grid over (tensor, used slot, 4 KB chunk);
-//                   one wave copies a chunk with 16-byte loads and
-//                   non-temporal stores.
-//   k_reduce_grad   persistent grid over (tensor, held expert, 4 KB chunk);
+//   k_prefetch_copy persistent grid over (tensor, slot, 8 KB chunk); items
+//                   of unused slots (-1) end at once, the others copy their
+//                   chunk with cached 16-byte loads and non-temporal stores.
+//   k_reduce_grad   persistent grid over (tensor, held expert, 2 KB chunk);
 //                   one wave loads the expert's chunk, adds the matching
 //                   slot chunks in ascending rank order (fp32, a + b), stores
 //                   the sum and clears the slot chunks.  Each slot has one
@@ -35,9 +36,16 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
 constexpr int kIndexThreads = 1024;
-constexpr int kChunkVec = 4;                       // 16-byte vectors per lane per chunk
-constexpr int kChunkBytes = kWave * kChunkVec * 16;  // 4 KB per wave item
+// Chosen by a sweep on MI355X.  The copy loads expert rows through the
+// caches: slots on several ranks often hold the same expert, and later
+// copies of it then hit in the cache (non-temporal loads were 1.5x slower).
+constexpr int kCopyVec = 8;          // 16-byte vectors per lane per copy chunk (8 KB per wave)
 constexpr int kCopyBlocks = 8192;
+constexpr bool kCopyNtLoad = false;
+constexpr bool kCopyNtStore = true;
+constexpr int kReduceVec = 2;        // 16-byte vectors per lane per reduction chunk (2 KB)
+constexpr int kReduceBlocks = 8192;
+constexpr bool kReduceNtLoad = true;
 
 struct TensorArgs {
   int32_t n;
@@ -109,33 +117,35 @@ __global__ void __launch_bounds__(kIndexThreads)
 }
 
 __global__ void __launch_bounds__(kThreads)
-    k_prefetch_copy(Dims d, PlanArrays pa, SlotIndex si, TensorArgs ta) {
+    k_prefetch_copy(Dims d, PlanArrays pa, TensorArgs ta) {
   if (pa.status[0] != 0) return;
   const int lane = threadIdx.x & (kWave - 1);
-  const int n_used = si.counts[0];
   const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   for (int t = 0; t < ta.n; ++t) {
     const int64_t V = ta.vecs[t];
-    const int64_t nch = (V + kWave * kChunkVec - 1) / (kWave * kChunkVec);
-    const int64_t items = (int64_t)n_used * nch;
+    const int64_t nch = (V + kWave * kCopyVec - 1) / (kWave * kCopyVec);
+    const int64_t items = (int64_t)d.R * d.B * nch;  // every slot; unused ones are skipped
     for (int64_t it = wave; it < items; it += nwaves) {
-      const int s = (int)(it / nch);
-      const int64_t c0 = (it - (int64_t)s * nch) * kWave * kChunkVec;
-      const int slot = si.used[s];
+      const int slot = (int)(it / nch);
+      const int64_t c0 = (it - (int64_t)slot * nch) * kWave * kCopyVec;
       const int e = pa.etc[slot];
+      if (e < 0) continue;
       const u32x4* sp = ta.src[t] + (int64_t)e * V;
       u32x4* dp = ta.dst[t] + (int64_t)slot * V;
-      u32x4 buf[kChunkVec];
+      u32x4 buf[kCopyVec];
 #pragma unroll
-      for (int c = 0; c < kChunkVec; ++c) {
+      for (int c = 0; c < kCopyVec; ++c) {
         const int64_t j = c0 + c * kWave + lane;
-        if (j < V) buf[c] = __builtin_nontemporal_load(sp + j);
+        if (j < V) buf[c] = kCopyNtLoad ? __builtin_nontemporal_load(sp + j) : sp[j];
       }
 #pragma unroll
-      for (int c = 0; c < kChunkVec; ++c) {
+      for (int c = 0; c < kCopyVec; ++c) {
         const int64_t j = c0 + c * kWave + lane;
-        if (j < V) __builtin_nontemporal_store(buf[c], dp + j);
+        if (j < V) {
+          if (kCopyNtStore) __builtin_nontemporal_store(buf[c], dp + j);
+          else dp[j] = buf[c];
+        }
       }
     }
   }
@@ -151,21 +161,21 @@ __global__ void __launch_bounds__(kThreads)
   const u32x4 zero = {0u, 0u, 0u, 0u};
   for (int t = 0; t < ta.n; ++t) {
     const int64_t V = ta.vecs[t];
-    const int64_t nch = (V + kWave * kChunkVec - 1) / (kWave * kChunkVec);
+    const int64_t nch = (V + kWave * kReduceVec - 1) / (kWave * kReduceVec);
     const int64_t items = (int64_t)n_act * nch;
     // src = expert gradient rows [E, V], dst = slot gradient rows [R, B, V]
     u32x4* grad = const_cast<u32x4*>(ta.src[t]);
     u32x4* slots = ta.dst[t];
     for (int64_t it = wave; it < items; it += nwaves) {
       const int a = (int)(it / nch);
-      const int64_t c0 = (it - (int64_t)a * nch) * kWave * kChunkVec;
+      const int64_t c0 = (it - (int64_t)a * nch) * kWave * kReduceVec;
       const int e = si.act_e[a];
       // lane u < R: the slot expert e holds on rank u (-1 if none)
       const int my_slot = lane < d.R ? si.act_match[a * d.R + lane] : -1;
       u32x4* gp = grad + (int64_t)e * V;
-      float acc[kChunkVec][4];
+      float acc[kReduceVec][4];
 #pragma unroll
-      for (int c = 0; c < kChunkVec; ++c) {
+      for (int c = 0; c < kReduceVec; ++c) {
         const int64_t j = c0 + c * kWave + lane;
         u32x4 v = zero;
         if (j < V) v = gp[j];
@@ -179,22 +189,22 @@ __global__ void __launch_bounds__(kThreads)
         const int j_slot = __builtin_amdgcn_readlane(my_slot, u);
         u32x4* sp = slots + ((int64_t)u * d.B + j_slot) * V;
 #pragma unroll
-        for (int c = 0; c < kChunkVec; ++c) {
+        for (int c = 0; c < kReduceVec; ++c) {
           const int64_t j = c0 + c * kWave + lane;
           if (j < V) {
-            const u32x4 v = __builtin_nontemporal_load(sp + j);
+            const u32x4 v = kReduceNtLoad ? __builtin_nontemporal_load(sp + j) : sp[j];
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[c][q] = acc[c][q] + __uint_as_float(v[q]);
           }
         }
 #pragma unroll
-        for (int c = 0; c < kChunkVec; ++c) {
+        for (int c = 0; c < kReduceVec; ++c) {
           const int64_t j = c0 + c * kWave + lane;
           if (j < V) __builtin_nontemporal_store(zero, sp + j);
         }
       }
 #pragma unroll
-      for (int c = 0; c < kChunkVec; ++c) {
+      for (int c = 0; c < kReduceVec; ++c) {
         const int64_t j = c0 + c * kWave + lane;
         if (j < V) {
           u32x4 v;
@@ -212,17 +222,17 @@ hipError_t launch_index(const Dims& d, const PlanArrays& pa, const SlotIndex& si
   return hipGetLastError();
 }
 
-int grid_for(const Dims& d, const TensorArgs& ta) {
-  // enough waves for every (used slot, chunk) item of the largest tensor,
-  // capped to a persistent grid
+int grid_for(const Dims& d, const TensorArgs& ta, int vec, int max_blocks) {
+  // enough waves for every (slot, chunk) item of the largest tensor, capped
+  // to a persistent grid
   int64_t most = 0;
   for (int t = 0; t < ta.n; ++t) {
-    const int64_t nch = (ta.vecs[t] + kWave * kChunkVec - 1) / (kWave * kChunkVec);
+    const int64_t nch = (ta.vecs[t] + kWave * vec - 1) / (kWave * vec);
     most = nch > most ? nch : most;
   }
   const int64_t waves = most * (int64_t)d.R * d.B;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  return (int)(blocks < kCopyBlocks ? (blocks > 0 ? blocks : 1) : kCopyBlocks);
+  return (int)(blocks < max_blocks ? (blocks > 0 ? blocks : 1) : max_blocks);
 }
 
 TensorArgs tensor_args(int n, const void* const* src, void* const* dst, const int64_t* bytes) {
@@ -241,10 +251,11 @@ TensorArgs tensor_args(int n, const void* const* src, void* const* dst, const in
 hipError_t launch_prefetch_weight(const Dims& d, const PlanArrays& pa, const SlotIndex& si, int n,
                                   const void* const* experts, void* const* slots,
                                   const int64_t* row_bytes, hipStream_t s) {
-  hipError_t e = launch_index(d, pa, si, s);
-  if (e != hipSuccess || d.B == 0) return e;
+  (void)si;  // the copy walks all slots itself; only the reduction needs the index
+  if (d.B == 0) return hipSuccess;
   const TensorArgs ta = tensor_args(n, experts, slots, row_bytes);
-  hipLaunchKernelGGL(k_prefetch_copy, dim3(grid_for(d, ta)), dim3(kThreads), 0, s, d, pa, si, ta);
+  hipLaunchKernelGGL(k_prefetch_copy, dim3(grid_for(d, ta, kCopyVec, kCopyBlocks)), dim3(kThreads),
+                     0, s, d, pa, ta);
   return hipGetLastError();
 }
 
@@ -255,7 +266,8 @@ hipError_t launch_reduce_grad(const Dims& d, const PlanArrays& pa, const SlotInd
   if (e != hipSuccess || d.B == 0) return e;
   const TensorArgs ta = tensor_args(n, reinterpret_cast<const void* const*>(grads),
                                     reinterpret_cast<void* const*>(slot_grads), row_bytes);
-  hipLaunchKernelGGL(k_reduce_grad, dim3(grid_for(d, ta)), dim3(kThreads), 0, s, d, pa, si, ta);
+  hipLaunchKernelGGL(k_reduce_grad, dim3(grid_for(d, ta, kReduceVec, kReduceBlocks)),
+                     dim3(kThreads), 0, s, d, pa, si, ta);
   return hipGetLastError();
 }
 
