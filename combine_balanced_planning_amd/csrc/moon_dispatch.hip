@@ -33,6 +33,7 @@ constexpr int kSliceVec = 2;       // 16-byte vectors per lane in a scatter slic
 constexpr int kZeroRows = 8;       // padding rows per zero-fill item
 constexpr int kScatterBlocks = 32768;  // persistent grids (a sweep of 2048, 8192, 32768)
 constexpr int kExpandBlocks = 32768;
+constexpr bool kScatterNtLoad = false;  // non-temporal: -1.8 % at r8-e64-k6, +1.6 % at DSv3
 // Half of the 256 MB last-level cache (MI355X): the largest token-row size
 // R*S*2H of a call for which the scatter caches the re-read primaries.
 constexpr int64_t kKeepBudgetBytes = 128ll << 20;
@@ -69,7 +70,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int c = 0; c < kSliceVec; ++c) {
         const int j = c0 + c * kWave + lane;
-        if (j < V) buf[c] = src[j];
+        if (j < V) buf[c] = kScatterNtLoad ? __builtin_nontemporal_load(src + j) : src[j];
       }
       if (status != 0) return;
       if (wlane) wwin[dst_global_row(dl)] = wk;
