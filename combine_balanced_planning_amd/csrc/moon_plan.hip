@@ -144,7 +144,6 @@ __device__ __forceinline__ void wave_tokens(const TileRange& tr, int w, int& ws0
 struct BalanceLds {
   int T[kMaxE], Pe[kMaxE];
   int L[kMaxR], keep[kMaxR], donor[kMaxR], segA[kMaxR], segB[kMaxR];
-  int pref[kPlanWaves][kMaxTiles + 1];       // a wave's tile prefix (histogram check)
   int nslot[kPlanWaves][kMaxSlotsPerRank];   // a wave's receiver slot sizes
   int flags;
 };
@@ -170,6 +169,7 @@ __global__ void __launch_bounds__(kPlanThreads)
   // loaded first, then their eight scans run back to back.
   for (int e0 = wave; e0 < E; e0 += kScanBatch * kPlanWaves) {
     int c[kScanBatch][kTilesPerLane];
+    int given[kScanBatch];  // lane r < R: tokens_per_expert[r][e], loaded with the counts
 #pragma unroll
     for (int j = 0; j < kScanBatch; ++j) {
       const int e = e0 + j * kPlanWaves;
@@ -179,6 +179,7 @@ __global__ void __launch_bounds__(kPlanThreads)
       c[j][1] = v.y;
       c[j][2] = v.z;
       c[j][3] = v.w;
+      given[j] = (tpe != nullptr && e < E && lane < R) ? tpe[lane * E + e] : 0;
     }
     int incl[kScanBatch];
 #pragma unroll
@@ -189,27 +190,28 @@ __global__ void __launch_bounds__(kPlanThreads)
       const int e = e0 + j * kPlanWaves;
       if (e >= E) break;
       int run = incl[j] - (c[j][0] + c[j][1] + c[j][2] + c[j][3]);
+      int ex[kTilesPerLane];  // exclusive prefix of e's routes at this lane's tiles
 #pragma unroll
       for (int s = 0; s < kTilesPerLane; ++s) {
         const int t = lane * kTilesPerLane + s;
+        ex[s] = run;
         if (t < nt) sc.base[e * nt + t] = run;
         run += c[j][s];
       }
-      if (lane == 0) L.T[e] = lane63(incl[j]);
+      const int total = lane63(incl[j]);
+      if (lane == 0) L.T[e] = total;
       if (tpe != nullptr) {
-        // routes of e from each source rank (a rank's tiles are consecutive)
-        int* rc = L.pref[wave];
-        for (int r = lane; r < R; r += kWave) rc[r] = 0;
-        wave_lds_fence();
-#pragma unroll
-        for (int s = 0; s < kTilesPerLane; ++s) {
-          const int t = lane * kTilesPerLane + s;
-          if (t < nt && c[j][s] != 0) atomicAdd(&rc[t / d.tiles_per_rank], c[j][s]);
-        }
-        wave_lds_fence();
-        for (int r = lane; r < R; r += kWave)
-          if (rc[r] != tpe[r * E + e]) atomicOr(&L.flags, kHistogram);
-        wave_lds_fence();
+        // A rank's tiles are consecutive, so its routes on e are the prefix
+        // at the next rank's first tile minus the prefix at its own.  Lane x
+        // fetches the prefix at tile x * tiles_per_rank (x <= R <= 32).
+        const int tile = min(lane, R) * d.tiles_per_rank;
+        const int src = min(tile / kTilesPerLane, kWave - 1), sub = tile % kTilesPerLane;
+        const int v0 = __shfl(ex[0], src, kWave), v1 = __shfl(ex[1], src, kWave);
+        const int v2 = __shfl(ex[2], src, kWave), v3 = __shfl(ex[3], src, kWave);
+        int pre = sub == 0 ? v0 : sub == 1 ? v1 : sub == 2 ? v2 : v3;
+        if (tile >= nt) pre = total;
+        const int next = __shfl_down(pre, 1, kWave);
+        if (lane < R && next - pre != given[j]) atomicOr(&L.flags, kHistogram);
       }
     }
   }
