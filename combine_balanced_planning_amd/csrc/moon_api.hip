@@ -7,6 +7,9 @@
 // MoonEPCommPlan arrays plus cu_seqlens and a status word.
 #include <new>
 
+#include <algorithm>
+#include <cmath>
+
 #include "moon_internal.h"
 
 namespace {
@@ -38,6 +41,12 @@ struct DeviceGuard {
   }
 };
 
+// Most planner tiles per call (never above kMaxTiles, nor the compute units).
+constexpr int kPlanTileCap = moon::kMaxTiles;
+// Cost of one more chunk per planner wave, in units of one expert count
+// scanned for one tile (fitted on MI355X over four workload shapes).
+constexpr double kChunkWeight = 30000.0;
+
 moon_status make_dims(const moon_config* c, Dims* d) {
   if (c == nullptr || c->flags != 0) return MOON_ERR_INVALID_ARG;
   if (c->R < 1 || c->E < 1 || c->K < 1 || c->S < 1 || c->H < 1 || c->token_padding < 1)
@@ -64,23 +73,35 @@ moon_status make_dims(const moon_config* c, Dims* d) {
   d->Eg = Eg;
   d->EB = c->E + B;
   d->NvS = (int32_t)nvs;
-  // Planner tiles: about kTileRoutes routes each, never across a rank
-  // boundary, at most one per compute unit and kMaxTiles in all.
-  int max_tiles = moon::kMaxTiles;
+  // Planner tiles, never across a rank boundary, at most one per compute
+  // unit and kMaxTiles in all.  The balance step scans E counts per tile in
+  // one workgroup, and each of a tile's kPlanWaves waves walks its share of
+  // the tile in chunks of floor(64/K) tokens, so plan time is about
+  // E*tiles + kChunkWeight*chunks (weight fitted on MI355X).  Tiles are a
+  // whole number of chunks per wave; the cheapest count is taken.
+  int max_tiles = kPlanTileCap;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       cus > 0 && cus < max_tiles)
     max_tiles = cus;
-  int tt = (moon::kTileRoutes + c->K - 1) / c->K;
-  if (tt > c->S) tt = c->S;
-  int tpr = (c->S + tt - 1) / tt;
-  if ((int64_t)c->R * tpr > max_tiles) {
-    tpr = max_tiles / c->R;
-    if (tpr < 1) tpr = 1;
-    tt = (c->S + tpr - 1) / tpr;
-    tpr = (c->S + tt - 1) / tt;
+  const int ctok = moon::kWave / c->K;
+  const int64_t round_tok = (int64_t)moon::kPlanWaves * ctok;  // tokens per chunk round
+  int tt = 0;
+  double best = 0.0;
+  for (int64_t m = 1; m <= (c->S + round_tok - 1) / round_tok; ++m) {
+    const int cand = (int)std::min<int64_t>(round_tok * m, c->S);
+    const int64_t tiles = (int64_t)c->R * ((c->S + cand - 1) / cand);
+    if (tiles > max_tiles) continue;
+    const double cost = (double)c->E * tiles + kChunkWeight * m;
+    if (tt == 0 || cost < best) {
+      tt = cand;
+      best = cost;
+    }
   }
+  if (tt == 0) tt = c->S;  // more ranks than compute units: one tile per rank
+  const int tpr = (c->S + tt - 1) / tt;
+  tt = (c->S + tpr - 1) / tpr;  // even out the tiles of a rank
   d->tile_tok = tt;
   d->tiles_per_rank = tpr;
   d->ntiles = c->R * tpr;

@@ -13,7 +13,6 @@ constexpr int kMaxR = 32;
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 64;
 constexpr int kMaxTiles = 256;      // up to four tiles per lane in the cross-tile scan
-constexpr int kTileRoutes = 768;    // routes per planner tile when there are enough tiles (sweep: 256-1024)
 constexpr int kPlanWaves = 16;      // waves per planner workgroup
 constexpr int kPlanThreads = kPlanWaves * kWave;
 constexpr int kMaxSlotsTotal = 8192;  // R * B

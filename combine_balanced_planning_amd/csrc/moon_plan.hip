@@ -6,12 +6,11 @@
 //  and How to set B: each rank ends with S*K routes, the excess going to
 //  redundant-expert slots whose experts all come from one remote home rank.)
 //
-// Three launches on the caller's stream.  Tiles of about 768 routes (more
-// when that would give more tiles than compute units) never span two source
-// ranks; a tile is one
-// workgroup of 16 waves; wave w owns a contiguous token range of its tile and
-// walks it in chunks of whole tokens (floor(64/K) tokens), so a token's K
-// routes sit in adjacent lanes.
+// Three launches on the caller's stream.  A tile is a token range of one
+// source rank (at most one tile per compute unit, sized by a cost model on
+// the host) and one workgroup of 16 waves; wave w owns a contiguous token
+// range of its tile and walks it in chunks of whole tokens (floor(64/K)
+// tokens), so a token's K routes sit in adjacent lanes.
 //
 //   k_plan_count    per tile: per-wave expert counts (LDS atomics) -> per-wave
 //                   prefixes and the tile's totals.
