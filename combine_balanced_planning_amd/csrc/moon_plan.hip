@@ -263,10 +263,11 @@ __global__ void __launch_bounds__(kPlanThreads)
         break;
       }
       const int o = __ffsll((unsigned long long)large) - 1;
-      const int f = C - __shfl(rem, u, kWave);
-      const int g_o = __shfl(given, o, kWave);
-      const int rem_o = __shfl(rem, o, kWave) - f;
-      const int cnt_o = __shfl(rcnt, o, kWave);
+      // u and o are uniform (taken from ballot masks): read their lanes directly
+      const int f = C - __builtin_amdgcn_readlane(rem, u);
+      const int g_o = __builtin_amdgcn_readlane(given, o);
+      const int rem_o = __builtin_amdgcn_readlane(rem, o) - f;
+      const int cnt_o = __builtin_amdgcn_readlane(rcnt, o);
       if (lane == u) {
         donor = o;
         take = f;
