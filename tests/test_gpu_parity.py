@@ -321,3 +321,51 @@ def test_hand_worked_examples(env, name):
     assert got["experts_to_copy"].tolist() == g["experts_to_copy"]
     start, n, end = pc.group_table(pt.gpu_plan_view(got, ref))
     assert n.tolist() == g["n"]
+
+
+def _random_case(i):
+    """A seeded random valid configuration: R, E = R * E/R, K, S, H (multiple
+    of 8, often not of 512 so slices end ragged), P, B (sometimes below E/R)
+    and a routing mode."""
+    rng = np.random.default_rng(1000 + i)
+    R = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 32]))
+    Eg = int(rng.integers(1, max(2, 512 // R // 4) + 1))
+    E = R * Eg
+    K = int(rng.integers(1, min(16, 64) + 1)) if rng.random() < 0.85 else int(rng.integers(17, 65))
+    S = int(rng.integers(1, 161))
+    H = 8 * int(rng.choice([1, 2, 17, 64, 65, 300, 896]))
+    P = int(rng.choice([1, 2, 3, 8, 16, 33]))
+    B = 0 if rng.random() < 0.7 else int(rng.integers(1, Eg + 1))
+    mode = str(rng.choice(["uniform", "skewed", "repeats", "home_block"]))
+    if mode in ("uniform", "skewed") and K > E:
+        mode = "repeats"
+    return R, E, K, S, H, B, P, mode
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_shapes(env, i):
+    """Seeded random shapes and routings, compared with the oracle in full;
+    when B < E/R makes the plan infeasible, the status must agree."""
+    moon, dev = env
+    R, E, K, S, H, B, P, mode = _random_case(i)
+    rng = np.random.default_rng(2000 + i)
+    topk = _edge_topk(rng, R, S, K, E, mode)
+    Bx = B if B > 0 else E // R
+    ref = oracle.plan(topk, E, Bx, P)
+    if ref.status == oracle.SLOT_BUDGET:
+        say(f"[case] random {i}: R={R} E={E} K={K} S={S} B={B} -> slot budget")
+        ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+        plan = moon.moon_plan_create(ctx)
+        try:
+            moon.moon_plan(ctx, pt.to_dev(topk, dev), None, plan)
+            assert moon.moon_plan_status(plan) == moon.MOON_ERR_SLOT_BUDGET
+        finally:
+            moon.moon_plan_destroy(plan)
+            moon.moon_ctx_destroy(ctx)
+        return
+    assert ref.status == oracle.OK
+    w = rng.random((R, S, K)).astype(np.float32)
+    hidden = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * S * H).reshape(R, S, H)
+    y = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * ref.NvS * H).reshape(R * ref.NvS, H)
+    run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, label=f"random-{i}-{mode}",
+             weighted=bool(i % 3))
