@@ -14,9 +14,9 @@
 //               (same page, Buffer.prefetch_weight)
 //   reduce    = add every slot gradient back into its expert's gradient row
 //               and clear the consumed slots (same page, Buffer.reduce_grad)
-// Arithmetic on values happens in combine (float64, the duplicate prologue's
-// fold in float32) and in the gradient reduction (float32, as the pages'
-// gradient tensors are).
+// Arithmetic on values happens in combine (float32 in the pages' order, with
+// a float64 counterpart as the exact reference) and in the gradient reduction
+// (float32, as the pages' gradient tensors are).
 
 #include "moon_oracle.h"
 
@@ -50,22 +50,32 @@ int64_t decode_row(int32_t d) { return d >= 0 ? (int64_t)d : -(int64_t)d - 1; }
 
 // One token: sum its K routed rows in ascending k, optionally scaled by the
 // route weight stored at the route's own row (Visual Guide, Buffer.combine:
-// each token's K contributions are reduced back into its row; the weights
-// are read back through the signed dst entries, both signs alike).
+// each token's K contributions are reduced back into its row, accumulated in
+// fp32; the weights are read back through the signed dst entries, both
+// signs alike).  `out` is the fp32 sum -- each product and each addition
+// rounded to fp32 in turn, ascending k -- rounded once to bf16; `acc`
+// receives the float64 sum of the same terms, the exact reference.
 template <class RowFn, class WFn>
 void combine_token(int32_t K, int32_t H, const int32_t* d, RowFn row, WFn wat, int32_t weighted,
                    uint16_t* out, float* wsk, double* acc) {
+  std::vector<float> sum32(H, 0.0f);
   std::vector<double> sum(H, 0.0);
   for (int k = 0; k < K; ++k) {
     int64_t G = decode_row(d[k]);
     const uint16_t* y = row(G);
     float wk = wat(G);
-    double c = weighted ? (double)wk : 1.0;
-    for (int h = 0; h < H; ++h) sum[h] += c * (double)bf16_to_float(y[h]);
+    float c32 = weighted ? wk : 1.0f;
+    double c = (double)c32;
+    for (int h = 0; h < H; ++h) {
+      float yv = bf16_to_float(y[h]);
+      float prod = c32 * yv;
+      sum32[h] = sum32[h] + prod;
+      sum[h] += c * (double)yv;
+    }
     if (wsk != nullptr) wsk[k] = wk;
   }
   for (int h = 0; h < H; ++h) {
-    out[h] = orc_bf16_from_double(sum[h]);
+    out[h] = orc_bf16_from_double((double)sum32[h]);
     if (acc != nullptr) acc[h] = sum[h];
   }
 }
@@ -78,12 +88,13 @@ void combine_token(int32_t K, int32_t H, const int32_t* d, RowFn row, WFn wat, i
 // row is bf16(sum over those routes, ascending k, of c_k * y) with the fp32
 // arithmetic the pages fix (separate multiply and add); it stands for all m
 // routes with coefficient 1.  The outer sum over primaries, ascending k, is
-// float64 and rounded once, as in the plain combine.  `fold(G, bits)`
-// receives every folded primary row.
+// fp32 as in the plain combine (`out`), with its float64 counterpart in
+// `acc`.  `fold(G, bits)` receives every folded primary row.
 template <class RowFn, class WFn, class FoldFn>
 void combine_token_prologue(int32_t K, int32_t H, int64_t NvS, const int32_t* d, RowFn row, WFn wat,
                             int32_t weighted, uint16_t* out, float* wsk, double* acc, FoldFn fold) {
   std::vector<double> sum(H, 0.0);
+  std::vector<float> sum32(H, 0.0f);
   std::vector<float> part(H);
   std::vector<uint16_t> bits(H);
   for (int k = 0; k < K; ++k) {
@@ -94,9 +105,14 @@ void combine_token_prologue(int32_t K, int32_t H, int64_t NvS, const int32_t* d,
     for (int k2 = k + 1; k2 < K; ++k2)
       if (d[k2] < 0 && decode_row(d[k2]) / NvS == G / NvS) members.push_back(k2);
     if (members.size() == 1) {
-      double c = weighted ? (double)wat(G) : 1.0;
+      float c32 = weighted ? wat(G) : 1.0f;
       const uint16_t* y = row(G);
-      for (int h = 0; h < H; ++h) sum[h] += c * (double)bf16_to_float(y[h]);
+      for (int h = 0; h < H; ++h) {
+        float yv = bf16_to_float(y[h]);
+        float prod = c32 * yv;
+        sum32[h] = sum32[h] + prod;
+        sum[h] += (double)c32 * (double)yv;
+      }
       continue;
     }
     std::fill(part.begin(), part.end(), 0.0f);
@@ -111,12 +127,15 @@ void combine_token_prologue(int32_t K, int32_t H, int64_t NvS, const int32_t* d,
     }
     for (int h = 0; h < H; ++h) {
       bits[h] = orc_bf16_from_double((double)part[h]);
-      sum[h] += (double)bf16_to_float(bits[h]);
+      float yv = bf16_to_float(bits[h]);
+      float prod = 1.0f * yv;
+      sum32[h] = sum32[h] + prod;
+      sum[h] += (double)yv;
     }
     fold(G, bits.data());
   }
   for (int h = 0; h < H; ++h) {
-    out[h] = orc_bf16_from_double(sum[h]);
+    out[h] = orc_bf16_from_double((double)sum32[h]);
     if (acc != nullptr) acc[h] = sum[h];
   }
 }

@@ -77,8 +77,10 @@ int32_t orc_row_sources(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B,
                         const int32_t* cu, int64_t* src);
 
 /* Combine over all tokens.  y [R*NvS,H] bf16 bits; wnvs [R*NvS] (needed when
- * weighted != 0).  out [R,S,H] bf16 bits; wsk_out [R,S,K] and acc [R,S,H]
- * (float64 sum before rounding) may be NULL. */
+ * weighted != 0).  out [R,S,H] bf16 bits: the fp32 sum of c_k * y_k, ascending
+ * k, every product and addition rounded to fp32, rounded once to bf16 (the
+ * pages accumulate combine in fp32).  wsk_out [R,S,K] and acc [R,S,H] (the
+ * float64 sum of the same terms, the exact reference) may be NULL. */
 int32_t orc_combine(int32_t R, int32_t K, int32_t S, int32_t H, int32_t NvS,
                     const int32_t* dst, const uint16_t* y, const float* wnvs,
                     int32_t weighted, uint16_t* out, float* wsk_out, double* acc);
@@ -95,8 +97,9 @@ int32_t orc_combine_rows(int32_t n, int32_t K, int32_t H, const int32_t* dst_tok
  * holding m >= 2 of its routes, the m rows are first summed in fp32
  * (ascending k, c_k = w_nvs[row] when weighted, else 1) and rounded to bf16
  * into the primary row; the main sum then takes primary routes only, a
- * folded primary with coefficient 1, in float64, rounded once.  folded
- * (may be NULL) [R*NvS,H] receives y with the folded primary rows. */
+ * folded primary with coefficient 1, in fp32 as orc_combine (acc: float64),
+ * rounded once.  folded (may be NULL) [R*NvS,H] receives y with the folded
+ * primary rows. */
 int32_t orc_combine_prologue(int32_t R, int32_t K, int32_t S, int32_t H, int32_t NvS,
                              const int32_t* dst, const uint16_t* y, const float* wnvs,
                              int32_t weighted, uint16_t* out, float* wsk_out, double* acc,

@@ -131,8 +131,15 @@ def test_weighted_combine_brute_force(case):
         ref[i // K] += np.float64(wwin[G[i]]) * _f32(y[G[i]]).astype(np.float64)
     assert np.allclose(acc.reshape(R * S, H), ref, rtol=1e-12, atol=1e-12)
     assert (wsk.view(np.uint32) == w.view(np.uint32)).all()
-    # out is the nearest bf16 to acc: no neighbour is closer
-    _assert_nearest_bf16(out, acc)
+    # out, the fp32 sum rounded to bf16, lies within the rounding of bf16
+    # plus the fp32 error of a K-term sum of the exact value
+    absum = np.zeros((R * S, H), np.float64)
+    for i in range(R * S * K):
+        absum[i // K] += abs(np.float64(wwin[G[i]])) * np.abs(_f32(y[G[i]]).astype(np.float64))
+    g = 1.01 * K * 2.0 ** -24
+    lim = 2.0 ** -8 * (np.abs(acc.reshape(R * S, H)) + g * absum) + g * absum + 1e-30
+    assert (np.abs(_f32(out).reshape(R * S, H).astype(np.float64) - acc.reshape(R * S, H))
+            <= lim).all()
 
 
 def test_combine_rows_matches_full_combine():
@@ -313,3 +320,61 @@ def test_prologue_rows_matches_full():
     assert (a2 == acc.reshape(R * S, H)[toks]).all()
     assert (w2 == wsk.reshape(R * S, K)[toks]).all()
     assert (f2 == folded[rows]).all()
+
+
+def _one_token_plan(K, E=8):
+    """R = 1, S = 1: a token whose K routes go to K distinct experts, so row
+    k of the window is route k's row (global route order within groups)."""
+    topk = np.arange(K, dtype=np.int32).reshape(1, 1, K)
+    pl = oracle.plan(topk, E, E, 1)
+    assert pl.status == oracle.OK
+    return pl
+
+
+def _rows_for(pl, vals):
+    """A window whose route rows hold the given bf16 bit patterns (H = 1)."""
+    y = np.zeros((pl.NvS, 1), np.uint16)
+    G = pc.decode(pl.dst).reshape(-1)
+    for k, v in enumerate(vals):
+        y[G[k], 0] = v
+    return y, G
+
+
+def test_combine_accumulates_in_fp32_in_ascending_k():
+    """Rows 2^24, 1, -2^24 (unweighted): in fp32, ascending k, 2^24 + 1 rounds
+    back to 2^24 (a tie, to even) and the sum is 0; the exact sum is 1."""
+    pl = _one_token_plan(3)
+    y, _ = _rows_for(pl, [0x4B80, 0x3F80, 0xCB80])  # 2^24, 1.0, -2^24 as bf16 bits
+    out, _, acc = oracle.combine(pl, y, None, weighted=False)
+    assert acc[0, 0, 0] == 1.0
+    assert out[0, 0, 0] == 0x0000
+
+
+def test_combine_rounds_product_and_sum_separately():
+    """c0 = 1, y0 = 1; c1 = 1 + 2^-23, y1 = 1 + 2^-7.  The product rounds to
+    1 + 2^-7 + 2^-23 (the 2^-30 term is below half an ulp); the sum
+    2 + 2^-7 + 2^-23 is a tie in fp32 and goes to even, 2 + 2^-7, which is a
+    tie in bf16 and goes to even, 2.0 (0x4000).  A fused multiply-add (or an
+    exact sum) keeps the 2^-30 and ends at 2 + 2^-6 (0x4001)."""
+    pl = _one_token_plan(2)
+    y, G = _rows_for(pl, [0x3F80, 0x3F81])  # 1.0, 1 + 2^-7
+    wnvs = np.zeros(pl.NvS, np.float32)
+    wnvs[G[0]] = 1.0
+    wnvs[G[1]] = np.float32(1.0 + 2.0 ** -23)
+    out, _, acc = oracle.combine(pl, y, wnvs, weighted=True)
+    assert out[0, 0, 0] == 0x4000
+    assert _bits(np.float32(acc[0, 0, 0]))[()] == 0x4001
+
+
+def test_combine_single_route_is_one_rounded_product():
+    """K = 1: out = bf16(fp32(c * y)), torch's conversion supplying the bf16."""
+    rng = np.random.default_rng(21)
+    pl = _one_token_plan(1)
+    for _ in range(50):
+        yb = _rand_bf16(rng, (1,))
+        c = np.float32(rng.random() * 3)
+        y, G = _rows_for(pl, [int(yb[0])])
+        wnvs = np.zeros(pl.NvS, np.float32)
+        wnvs[G[0]] = c
+        out, _, _ = oracle.combine(pl, y, wnvs, weighted=True)
+        assert out[0, 0, 0] == _bits(np.array([c * _f32(yb)[0]], np.float32))[0]

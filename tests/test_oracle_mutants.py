@@ -31,7 +31,18 @@ MUTANTS = {
     "dup_loff_begin_wrong": ("rec[1] = (int32_t)nd;", "rec[1] = (int32_t)ng;"),
     "route_weight_of_first_k": ("if (w != nullptr) wwin[G] = w[t * K + k];",
                                 "if (w != nullptr) wwin[G] = w[t * K];"),
-    "combine_drops_weight": ("double c = weighted ? (double)wk : 1.0;", "double c = 1.0;"),
+    "combine_drops_weight": ("float c32 = weighted ? wk : 1.0f;", "float c32 = 1.0f;"),
+    "combine_fused_multiply_add": ("      sum32[h] = sum32[h] + prod;\n      sum[h] += c * (double)yv;",
+                                   "      sum32[h] = std::fma(c32, yv, sum32[h]);\n"
+                                   "      sum[h] += c * (double)yv;"),
+    "combine_output_from_float64": ("    if (wsk != nullptr) wsk[k] = wk;\n  }\n  for (int h = 0; h < H; ++h) {\n"
+                                    "    out[h] = orc_bf16_from_double((double)sum32[h]);",
+                                    "    if (wsk != nullptr) wsk[k] = wk;\n  }\n  for (int h = 0; h < H; ++h) {\n"
+                                    "    out[h] = orc_bf16_from_double(sum[h]);"),
+    "combine_descending_k": ("  for (int k = 0; k < K; ++k) {\n    int64_t G = decode_row(d[k]);\n"
+                             "    const uint16_t* y = row(G);",
+                             "  for (int k = K - 1; k >= 0; --k) {\n    int64_t G = decode_row(d[k]);\n"
+                             "    const uint16_t* y = row(G);"),
     "dst_decode_off_by_one": ("return d >= 0 ? (int64_t)d : -(int64_t)d - 1;",
                               "return d >= 0 ? (int64_t)d : -(int64_t)d;"),
     "rounding_truncates": ("double r = std::nearbyint(scaled);", "double r = std::trunc(scaled);"),
