@@ -53,8 +53,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 __device__ __forceinline__ const int32_t* group_record(const Dims& d, const PlanArrays& pa,
                                                       int lane, int cnt, int incl, int gi,
                                                       int* u_out) {
-  const int u = __popcll(__ballot(lane < d.R && incl <= gi));
-  const int first = __shfl(incl - cnt, u, kWave);
+  const int u = __popcll(__ballot(lane < d.R && incl <= gi));  // uniform
+  const int first = __builtin_amdgcn_readlane(incl - cnt, u);
   *u_out = u;
   return pa.dup_groups + ((int64_t)u * d.NvS + (gi - first)) * 3;
 }
@@ -67,13 +67,8 @@ __global__ void __launch_bounds__(kThreads)
   const int V = d.H / 8;
   const int nsl = (V + kWave - 1) / kWave;
   const int cnt = lane < d.R ? pa.dup_counts[lane * 2] : 0;
-  int incl = cnt;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += t;
-  }
-  const int64_t items = (int64_t)__shfl(incl, kWave - 1, kWave) * nsl;
+  const int incl = wave_incl_scan(cnt);
+  const int64_t items = (int64_t)__builtin_amdgcn_readlane(incl, kWave - 1) * nsl;
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t it = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; it < items;
        it += nwaves) {

@@ -139,13 +139,8 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays
   // (The counts are loaded alongside the plan's status word.)
   const int c = lane < d.R ? pa.dup_counts[lane * 2] : 0;
   if (pa.status[0] != 0) return;
-  int incl = c;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += t;
-  }
-  const int64_t items = (int64_t)__shfl(incl, kWave - 1, kWave) * nsl;
+  const int incl = wave_incl_scan(c);
+  const int64_t items = (int64_t)__builtin_amdgcn_readlane(incl, kWave - 1) * nsl;
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t it0 = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; it0 < items;
        it0 += nwaves * UI) {
@@ -161,8 +156,8 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays
       loff[i] = 0;
       if (it < items) {
         const int gi = (int)(it / nsl), sl = (int)(it - (int64_t)gi * nsl);
-        const int u = __popcll(__ballot(lane < d.R && incl <= gi));
-        const int first = __shfl(incl - c, u, kWave);
+        const int u = __popcll(__ballot(lane < d.R && incl <= gi));  // uniform
+        const int first = __builtin_amdgcn_readlane(incl - c, u);
         const int32_t* rec = pa.dup_groups + ((int64_t)u * d.NvS + (gi - first)) * 3;
         base[i] = (int64_t)u * d.NvS;
         prow[i] = rec[0];

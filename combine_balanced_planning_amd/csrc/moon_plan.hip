@@ -57,18 +57,6 @@ __device__ __forceinline__ uint64_t below_lane(int l) {
 
 __device__ __forceinline__ uint64_t lanes_below() { return below_lane(lane_id()); }
 
-// Inclusive prefix sum over the 64 lanes with DPP: shifts within rows of 16
-// lanes, then row broadcasts of lanes 15 and 31.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31
-  return v;
-}
-
 __device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(v, kWave - 1); }
 
 __device__ __forceinline__ int wave_sum(int v) { return lane63(wave_incl_scan(v)); }
