@@ -39,6 +39,8 @@ namespace {
 
 constexpr int kBatch = 16;            // chunks a wave stages in LDS at once
 constexpr int kCuLds = 8192;          // cu_seqlens entries staged in LDS when they fit
+static_assert(kMaxE <= kPlanThreads && kMaxR <= kPlanThreads && kCuLds % kPlanThreads == 0,
+              "placement stages one table element per thread");
 constexpr int kScanBatch = 8;         // experts whose tile counts a wave loads at once
 constexpr int kTilesPerLane = kMaxTiles / kWave;
 constexpr int kMaxSlotsPerRank = kMaxE / 2;  // pieces per receiver <= E/R <= E/2 (R >= 2)
@@ -84,24 +86,6 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
   __builtin_amdgcn_wave_barrier();
-}
-
-// n values from global memory into LDS, eight loads in flight per thread.
-__device__ __forceinline__ void stage_lds(int* __restrict__ dst, const int32_t* __restrict__ src,
-                                          int n) {
-  for (int x0 = 0; x0 < n; x0 += 8 * kPlanThreads) {
-    int v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int x = x0 + j * kPlanThreads + threadIdx.x;
-      v[j] = x < n ? src[x] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int x = x0 + j * kPlanThreads + threadIdx.x;
-      if (x < n) dst[x] = v[j];
-    }
-  }
 }
 
 struct TileRange {
@@ -470,18 +454,46 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, cons
       const int nl = (c < nchunks) ? min(ctok, ws1 - tok) * K : 0;
       v[c] = lane < nl ? topk[(rowbase + tok) * K + lane] : -1;
     }
-    stage_lds(L.Pe, sc.Pe, E);
-    stage_lds(L.slot, sc.slot_of, E);
-    for (int e = threadIdx.x; e < E; e += kPlanThreads) L.base[e] = sc.base[e * nt + t];
-    if (kCuInLds) stage_lds(L.cu, pa.cu, R * EB);
-    if (threadIdx.x < R) {
-      const int h = threadIdx.x;
-      L.keep[h] = sc.keep[h];
-      L.segA[h] = sc.seg_a[h];
-      L.segB[h] = sc.seg_b[h];
-      L.recv[h] = sc.recv[h];
-      L.rfirst[h] = sc.recv_first[h];
-      L.rcnt[h] = sc.recv_cnt[h];
+    // Every table element this thread stages (E <= kMaxE <= kPlanThreads, so
+    // one per expert array; R*EB <= kCuLds) is loaded before any is stored,
+    // so the loads share one memory round trip.
+    const int me = threadIdx.x;
+    const bool xe = me < E, xr = me < R;
+    const int pe = xe ? sc.Pe[me] : 0;
+    const int so = xe ? sc.slot_of[me] : 0;
+    const int bs = xe ? sc.base[me * nt + t] : 0;
+    int cuv[kCuLds / kPlanThreads];
+#pragma unroll
+    for (int i = 0; i < kCuLds / kPlanThreads; ++i) {
+      const int j = me + i * kPlanThreads;
+      cuv[i] = (kCuInLds && j < R * EB) ? pa.cu[j] : 0;
+    }
+    int kp = 0, sa = 0, sb = 0, rv = 0, rf = 0, rc = 0;
+    if (xr) {
+      kp = sc.keep[me];
+      sa = sc.seg_a[me];
+      sb = sc.seg_b[me];
+      rv = sc.recv[me];
+      rf = sc.recv_first[me];
+      rc = sc.recv_cnt[me];
+    }
+    if (xe) {
+      L.Pe[me] = pe;
+      L.slot[me] = so;
+      L.base[me] = bs;
+    }
+#pragma unroll
+    for (int i = 0; i < kCuLds / kPlanThreads; ++i) {
+      const int j = me + i * kPlanThreads;
+      if (kCuInLds && j < R * EB) L.cu[j] = cuv[i];
+    }
+    if (xr) {
+      L.keep[me] = kp;
+      L.segA[me] = sa;
+      L.segB[me] = sb;
+      L.recv[me] = rv;
+      L.rfirst[me] = rf;
+      L.rcnt[me] = rc;
     }
     for (int x = threadIdx.x; x < kPlanWaves * E; x += kPlanThreads) L.run[x] = 0;
     for (int x = threadIdx.x; x < kPlanWaves * R * 2; x += kPlanThreads) L.wc[x] = 0;
