@@ -44,8 +44,9 @@ struct DeviceGuard {
 // Most planner tiles per call (never above kMaxTiles, nor the compute units).
 constexpr int kPlanTileCap = moon::kMaxTiles;
 // Cost of one more chunk per planner wave, in units of one expert count
-// scanned for one tile (fitted on MI355X over four workload shapes).
-constexpr double kChunkWeight = 30000.0;
+// reduced for one tile (fitted on MI355X over five workload shapes: a chunk
+// costs about 3 us, a tile's share of the count matrix very little).
+constexpr double kChunkWeight = 300000.0;
 
 moon_status make_dims(const moon_config* c, Dims* d) {
   if (c == nullptr || c->flags != 0) return MOON_ERR_INVALID_ARG;
@@ -74,9 +75,9 @@ moon_status make_dims(const moon_config* c, Dims* d) {
   d->EB = c->E + B;
   d->NvS = (int32_t)nvs;
   // Planner tiles, never across a rank boundary, at most one per compute
-  // unit and kMaxTiles in all.  The balance step scans E counts per tile in
-  // one workgroup, and each of a tile's kPlanWaves waves walks its share of
-  // the tile in chunks of floor(64/K) tokens, so plan time is about
+  // unit and kMaxTiles in all.  Every tile reduces the E x tiles count
+  // matrix, and each of its kPlanWaves waves walks its share of the tile in
+  // chunks of floor(64/K) tokens, so plan time is about
   // E*tiles + kChunkWeight*chunks (weight fitted on MI355X).  Tiles are a
   // whole number of chunks per wave; the cheapest count is taken.
   int max_tiles = kPlanTileCap;
@@ -204,14 +205,6 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   size_t off = 0;
   const size_t i4 = sizeof(int32_t);
   const size_t o_cnt = carve(off, (size_t)(d.E + 1) * d.ntiles_pad * i4);
-  const size_t o_base = carve(off, (size_t)d.E * d.ntiles * i4);
-  const size_t o_pe = carve(off, (size_t)d.E * i4);
-  const size_t o_keep = carve(off, (size_t)d.R * i4);
-  const size_t o_donor = carve(off, (size_t)d.R * i4);
-  const size_t o_sa = carve(off, (size_t)d.R * i4);
-  const size_t o_sb = carve(off, (size_t)d.R * i4);
-  const size_t o_slot = carve(off, (size_t)d.E * i4);
-  const size_t o_recv = carve(off, (size_t)d.R * 3 * i4);
   const size_t o_agg = carve(off, (size_t)d.ntiles * d.R * 8);
   const size_t o_epoch = carve(off, i4);
   const size_t o_used = carve(off, (size_t)d.R * d.B * i4);
@@ -232,16 +225,6 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
   }
   char* b = static_cast<char*>(c->scratch_mem);
   c->sc.tile_cnt = reinterpret_cast<int32_t*>(b + o_cnt);
-  c->sc.base = reinterpret_cast<int32_t*>(b + o_base);
-  c->sc.Pe = reinterpret_cast<int32_t*>(b + o_pe);
-  c->sc.keep = reinterpret_cast<int32_t*>(b + o_keep);
-  c->sc.donor = reinterpret_cast<int32_t*>(b + o_donor);
-  c->sc.seg_a = reinterpret_cast<int32_t*>(b + o_sa);
-  c->sc.seg_b = reinterpret_cast<int32_t*>(b + o_sb);
-  c->sc.slot_of = reinterpret_cast<int32_t*>(b + o_slot);
-  c->sc.recv = reinterpret_cast<int32_t*>(b + o_recv);
-  c->sc.recv_first = c->sc.recv + d.R;
-  c->sc.recv_cnt = c->sc.recv + 2 * d.R;
   c->sc.tile_agg = reinterpret_cast<uint64_t*>(b + o_agg);
   c->sc.epoch = reinterpret_cast<uint32_t*>(b + o_epoch);
   c->si.used = reinterpret_cast<int32_t*>(b + o_used);

@@ -39,16 +39,6 @@ struct Dims {
 struct Scratch {
   int32_t* tile_cnt;     // [E+1][ntiles_pad] routes of expert e in tile t; row E holds 1
                          // for a tile with an id outside [0,E); padding columns stay 0
-  int32_t* base;         // [E][ntiles] routes of e in earlier tiles (global route order)
-  int32_t* Pe;           // [E] start of expert e in its home rank's stream
-  int32_t* keep;         // [R] routes a rank keeps from its own stream
-  int32_t* donor;        // [R] rank a receiver takes from (-1 if none)
-  int32_t* seg_a;        // [R] receiver's segment [seg_a, seg_b) of its donor's stream
-  int32_t* seg_b;        // [R]
-  int32_t* slot_of;      // [R][Eg] slot of the donor's j-th expert on receiver u (-1)
-  int32_t* recv;         // [R] receivers in the order they were served (grouped by donor)
-  int32_t* recv_first;   // [R] index in recv of a donor's first receiver
-  int32_t* recv_cnt;     // [R] receivers of a donor
   uint64_t* tile_agg;    // [ntiles][R] packed (tag, duplicate groups, duplicate rows) per rank
   uint32_t* epoch;       // [1] tag of the latest planning call
 };

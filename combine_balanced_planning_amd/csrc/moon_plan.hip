@@ -6,26 +6,33 @@
 //  and How to set B: each rank ends with S*K routes, the excess going to
 //  redundant-expert slots whose experts all come from one remote home rank.)
 //
-// Three launches on the caller's stream.  A tile is a token range of one
+// Two launches on the caller's stream.  A tile is a token range of one
 // source rank (at most one tile per compute unit, sized by a cost model on
 // the host) and one workgroup of 16 waves; wave w owns a contiguous token
 // range of its tile and walks it in chunks of whole tokens (floor(64/K)
 // tokens), so a token's K routes sit in adjacent lanes.
 //
-//   k_plan_count    per tile: per-wave expert counts (LDS atomics) -> per-wave
-//                   prefixes and the tile's totals.
-//   k_plan_balance  one workgroup: per-expert scans over tiles (16-byte rows,
-//                   a lane per four tiles), home stream offsets, the alias
-//                   fill over the R rank loads (one wave, one lane per rank),
-//                   then per rank its slots and padded layout.
-//   k_plan_place    per tile: stable rank of every route = tile base + wave
-//                   prefix + running per-wave counter + rank inside the chunk
-//                   (ballot match over the expert-id bits); stream position
-//                   -> (destination rank, group, row); primary or duplicate by
-//                   a ballot match over (token, destination rank); signed dst.
-//                   Each tile publishes its duplicate counts per rank and
-//                   reads those of the earlier tiles (never of later ones, so
-//                   the wait always ends); then the duplicate records.
+//   k_plan_count    per tile: expert counts (LDS atomics) -> one column of
+//                   the [E][tiles] count matrix.
+//   k_plan_place    per tile, in LDS:
+//                   - balance, recomputed by every tile from the count
+//                     matrix (identical in all of them, so no tile waits for
+//                     another): expert totals and the tile's own base (routes
+//                     of each expert in earlier tiles), home stream offsets,
+//                     the alias fill over the R rank loads (one wave, one lane
+//                     per rank), then per rank its slots and the start rows of
+//                     its padded groups; tile u also writes rank u's
+//                     experts_to_copy, remote_stats, cu_seqlens and
+//                     zero_fill_ranges;
+//                   - placement: stable rank of every route = tile base + wave
+//                     prefix + running per-wave counter + rank inside the chunk
+//                     (ballot match over the expert-id bits); stream position
+//                     -> (destination rank, group, row); primary or duplicate
+//                     by a ballot match over (token, destination rank); signed
+//                     dst;
+//                   - duplicate records: each tile publishes its duplicate
+//                     counts per rank and reads those of the earlier tiles
+//                     (never of later ones, so the wait always ends).
 //
 // The few words tiles pass to each other inside k_plan_place are relaxed
 // atomics at agent scope carrying the call's tag in their high half: coherent
@@ -38,12 +45,11 @@ namespace moon {
 namespace {
 
 constexpr int kBatch = 16;            // chunks a wave stages in LDS at once
-constexpr int kCuLds = 8192;          // cu_seqlens entries staged in LDS when they fit
-static_assert(kMaxE <= kPlanThreads && kMaxR <= kPlanThreads && kCuLds % kPlanThreads == 0,
-              "placement stages one table element per thread");
+static_assert(kMaxE <= kPlanThreads, "one thread per expert in the table passes");
+static_assert(kMaxE / kPlanWaves <= 32, "checked expert groups form a 32-bit mask");
 constexpr int kScanBatch = 8;         // experts whose tile counts a wave loads at once
 constexpr int kTilesPerLane = kMaxTiles / kWave;
-constexpr int kMaxSlotsPerRank = kMaxE / 2;  // pieces per receiver <= E/R <= E/2 (R >= 2)
+static_assert(kTilesPerLane == 4, "a lane holds four tiles of a count row (one 16-byte load)");
 constexpr uint32_t kSpinLimit = 1u << 24;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
@@ -110,248 +116,8 @@ __device__ __forceinline__ void wave_tokens(const TileRange& tr, int w, int& ws0
 }
 
 // ---------------------------------------------------------------------------
-// Balance: one workgroup (kept apart from k_plan_count: finishing the counts
-// with fences and letting the last workgroup balance measured 7 us slower).
-struct BalanceLds {
-  int T[kMaxE], Pe[kMaxE];
-  int L[kMaxR], keep[kMaxR], donor[kMaxR], segA[kMaxR], segB[kMaxR];
-  int nslot[kPlanWaves][kMaxSlotsPerRank];   // a wave's receiver slot sizes
-  int flags;
-};
-
 __global__ void __launch_bounds__(kPlanThreads)
-    k_plan_balance(Dims d, const int32_t* __restrict__ tpe, Scratch sc, PlanArrays pa) {
-  __shared__ BalanceLds L;
-  const int lane = lane_id(), wave = wave_id();
-  const int E = d.E, R = d.R, Eg = d.Eg, B = d.B, EB = d.EB, nt = d.ntiles, ntp = d.ntiles_pad;
-  if (threadIdx.x == 0) L.flags = 0;
-  __syncthreads();
-
-  // Ids outside [0, E) anywhere?  (row E of the tile counts)
-  if (wave == 0) {
-    int4 b = {0, 0, 0, 0};
-    if (lane * 4 < nt) b = *reinterpret_cast<const int4*>(sc.tile_cnt + E * ntp + lane * 4);
-    if (__ballot((b.x | b.y | b.z | b.w) != 0) && lane == 0) atomicOr(&L.flags, kBadExpert);
-  }
-
-  // Phase A: per-expert exclusive scan over tiles (tile order = global route
-  // order; lane l holds tiles 4l..4l+3, one 16-byte load) and expert totals.
-  // Wave w takes experts w, w+16, ..; a batch of eight experts' rows is
-  // loaded first, then their eight scans run back to back.
-  for (int e0 = wave; e0 < E; e0 += kScanBatch * kPlanWaves) {
-    int c[kScanBatch][kTilesPerLane];
-    int given[kScanBatch];  // lane r < R: tokens_per_expert[r][e], loaded with the counts
-#pragma unroll
-    for (int j = 0; j < kScanBatch; ++j) {
-      const int e = e0 + j * kPlanWaves;
-      int4 v = {0, 0, 0, 0};
-      if (e < E && lane * 4 < nt) v = *reinterpret_cast<const int4*>(sc.tile_cnt + e * ntp + lane * 4);
-      c[j][0] = v.x;
-      c[j][1] = v.y;
-      c[j][2] = v.z;
-      c[j][3] = v.w;
-      given[j] = (tpe != nullptr && e < E && lane < R) ? tpe[lane * E + e] : 0;
-    }
-    int incl[kScanBatch];
-#pragma unroll
-    for (int j = 0; j < kScanBatch; ++j)
-      incl[j] = wave_incl_scan(c[j][0] + c[j][1] + c[j][2] + c[j][3]);
-#pragma unroll
-    for (int j = 0; j < kScanBatch; ++j) {
-      const int e = e0 + j * kPlanWaves;
-      if (e >= E) break;
-      int run = incl[j] - (c[j][0] + c[j][1] + c[j][2] + c[j][3]);
-      int ex[kTilesPerLane];  // exclusive prefix of e's routes at this lane's tiles
-#pragma unroll
-      for (int s = 0; s < kTilesPerLane; ++s) {
-        const int t = lane * kTilesPerLane + s;
-        ex[s] = run;
-        if (t < nt) sc.base[e * nt + t] = run;
-        run += c[j][s];
-      }
-      const int total = lane63(incl[j]);
-      if (lane == 0) L.T[e] = total;
-      if (tpe != nullptr) {
-        // A rank's tiles are consecutive, so its routes on e are the prefix
-        // at the next rank's first tile minus the prefix at its own.  Lane x
-        // fetches the prefix at tile x * tiles_per_rank (x <= R <= 32).
-        const int tile = min(lane, R) * d.tiles_per_rank;
-        const int src = min(tile / kTilesPerLane, kWave - 1), sub = tile % kTilesPerLane;
-        const int v0 = __shfl(ex[0], src, kWave), v1 = __shfl(ex[1], src, kWave);
-        const int v2 = __shfl(ex[2], src, kWave), v3 = __shfl(ex[3], src, kWave);
-        int pre = sub == 0 ? v0 : sub == 1 ? v1 : sub == 2 ? v2 : v3;
-        if (tile >= nt) pre = total;
-        const int next = __shfl_down(pre, 1, kWave);
-        if (lane < R && next - pre != given[j]) atomicOr(&L.flags, kHistogram);
-      }
-    }
-  }
-  __syncthreads();
-  // Stream offsets: home rank h's stream is its experts in ascending id.
-  for (int h = wave; h < R; h += kPlanWaves) {
-    int carry = 0;
-    for (int j0 = 0; j0 < Eg; j0 += kWave) {
-      const int j = j0 + lane;
-      const int v = j < Eg ? L.T[h * Eg + j] : 0;
-      const int incl = wave_incl_scan(v);
-      if (j < Eg) {
-        L.Pe[h * Eg + j] = carry + incl - v;
-        sc.Pe[h * Eg + j] = carry + incl - v;
-      }
-      carry += lane63(incl);
-    }
-    if (lane == 0) L.L[h] = carry;
-  }
-  __syncthreads();
-  if (L.flags & kBadExpert) {
-    if (threadIdx.x == 0) pa.status[0] = L.flags;
-    return;
-  }
-
-  // Phase B, one wave, lane = rank: the alias fill.  Under-loaded ranks, in
-  // ascending order, take what they lack from the lowest over-loaded rank; a
-  // donor pushed below S*K joins the back of the receiver queue.  Donors are
-  // used up in ascending order, so the appended receivers come after all
-  // initial ones and in ascending order too: both queues are bit masks.
-  if (wave == 0) {
-    const int C = d.S * d.K;
-    int rem = lane < R ? L.L[lane] : C;
-    int donor = -1, take = 0, off = 0, given = 0;
-    int recv = 0, rfirst = 0, rcnt = 0;  // lane j: j-th receiver served; lane o: donor o's range
-    uint64_t small = __ballot(rem < C), large = __ballot(rem > C), appended = 0;
-    int served = 0;
-    bool broken = false;
-    while (small | appended) {
-      int u;
-      if (small) {
-        u = __ffsll((unsigned long long)small) - 1;
-        small &= small - 1;
-      } else {
-        u = __ffsll((unsigned long long)appended) - 1;
-        appended &= appended - 1;
-      }
-      if (!large) {  // cannot happen: the loads sum to R*C
-        broken = true;
-        break;
-      }
-      const int o = __ffsll((unsigned long long)large) - 1;
-      // u and o are uniform (taken from ballot masks): read their lanes directly
-      const int f = C - __builtin_amdgcn_readlane(rem, u);
-      const int g_o = __builtin_amdgcn_readlane(given, o);
-      const int rem_o = __builtin_amdgcn_readlane(rem, o) - f;
-      const int cnt_o = __builtin_amdgcn_readlane(rcnt, o);
-      if (lane == u) {
-        donor = o;
-        take = f;
-        off = g_o;
-      }
-      if (lane == o) {
-        given = g_o + f;
-        rem = rem_o;
-        if (cnt_o == 0) rfirst = served;
-        rcnt = cnt_o + 1;
-      }
-      if (lane == served) recv = u;
-      ++served;
-      if (rem_o < C) {
-        large &= large - 1;
-        appended |= 1ull << o;
-      } else if (rem_o == C) {
-        large &= large - 1;
-      }
-    }
-    if (broken && lane == 0) atomicOr(&L.flags, kInternal);
-    const int keep = rem;
-    const int dk = __shfl(keep, donor < 0 ? 0 : donor, kWave);
-    const int sa = donor >= 0 ? dk + off : 0;
-    const int sb = donor >= 0 ? dk + off + take : 0;
-    if (lane < R) {
-      L.keep[lane] = keep;
-      L.donor[lane] = donor;
-      L.segA[lane] = sa;
-      L.segB[lane] = sb;
-      sc.keep[lane] = keep;
-      sc.donor[lane] = donor;
-      sc.seg_a[lane] = sa;
-      sc.seg_b[lane] = sb;
-      sc.recv[lane] = recv;
-      sc.recv_first[lane] = rfirst;
-      sc.recv_cnt[lane] = rcnt;
-    }
-  }
-  __syncthreads();
-
-  // Phase C, one wave per rank u: its slots as a receiver (the donor's
-  // experts overlapping its segment, ascending id, from slot 0), then the
-  // padded layout of its E+B groups.
-  for (int u = wave; u < R; u += kPlanWaves) {
-    const int o = L.donor[u];
-    int count = 0, routed = 0;
-    for (int j0 = 0; j0 < Eg; j0 += kWave) {
-      const int j = j0 + lane;
-      bool piece = false;
-      int len = 0;
-      if (o >= 0 && j < Eg) {
-        const int e = o * Eg + j;
-        const int lo = max(L.Pe[e], L.segA[u]);
-        const int hi = min(L.Pe[e] + L.T[e], L.segB[u]);
-        piece = L.T[e] > 0 && lo < hi;
-        len = hi - lo;
-      }
-      const uint64_t m = __ballot(piece);
-      const int slot = count + __popcll(m & lanes_below());
-      const bool kept = piece && slot < B && slot < kMaxSlotsPerRank;
-      if (j < Eg) sc.slot_of[u * Eg + j] = kept ? slot : -1;
-      if (kept) {
-        pa.etc[u * B + slot] = o * Eg + j;
-        L.nslot[wave][slot] = len;
-        routed += len;
-      } else if (piece) {
-        atomicOr(&L.flags, kSlotBudget);
-      }
-      count += __popcll(m);
-    }
-    routed = wave_sum(routed);
-    const int used = min(count, B);
-    for (int j = used + lane; j < B; j += kWave) pa.etc[u * B + j] = -1;
-    if (lane == 0) {
-      pa.rstats[u * 2 + 0] = used;
-      pa.rstats[u * 2 + 1] = routed;
-    }
-    wave_lds_fence();
-    if (count > B) continue;  // slot budget exceeded: no layout for this plan
-    int carry = 0;
-    const int P = d.P;
-    for (int g0 = 0; g0 < EB; g0 += kWave) {
-      const int g = g0 + lane;
-      int n = 0;
-      if (g < E) {
-        if (g / Eg == u) n = min(max(L.keep[u] - L.Pe[g], 0), L.T[g]);
-      } else if (g < EB && g - E < used) {
-        n = L.nslot[wave][g - E];
-      }
-      const int pad = n == 0 ? 0 : (n + P - 1) / P * P;
-      const int incl = wave_incl_scan(pad);
-      if (g < EB) {
-        const int end = carry + incl;
-        pa.cu[u * EB + g] = end;
-        pa.zfr[(u * EB + g) * 2 + 0] = end - pad + n;
-        pa.zfr[(u * EB + g) * 2 + 1] = end;
-      }
-      carry += lane63(incl);
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    pa.status[0] = L.flags;
-    const uint32_t next = sc.epoch[0] + 1u;  // tag of this call's words in k_plan_place
-    sc.epoch[0] = next == 0u ? 1u : next;
-  }
-}
-
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kPlanThreads)
-    k_plan_count(Dims d, const int32_t* __restrict__ topk, Scratch sc) {
+    k_plan_count(Dims d, const int32_t* __restrict__ topk, Scratch sc, PlanArrays pa) {
   __shared__ int cnt[kMaxE];
   __shared__ int sBad;
   const int E = d.E;
@@ -376,6 +142,11 @@ __global__ void __launch_bounds__(kPlanThreads)
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPlanThreads) sc.tile_cnt[e * d.ntiles_pad + t] = cnt[e];
   if (threadIdx.x == 0) sc.tile_cnt[E * d.ntiles_pad + t] = sBad;
+  if (t == 0 && threadIdx.x == 0) {
+    pa.status[0] = 0;  // k_plan_place ORs in what it finds
+    const uint32_t next = sc.epoch[0] + 1u;  // tag of this call's words in k_plan_place
+    sc.epoch[0] = next == 0u ? 1u : next;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -406,32 +177,266 @@ __device__ __forceinline__ uint64_t match_bits(uint64_t set, int key, int bits) 
   return peers;
 }
 
-struct PlaceLds {
+struct PlanLds {
   int run[kPlanWaves * kMaxE];             // per-wave counts, then running positions
   int stage[kPlanWaves * kBatch * kWave];  // a wave's staged expert ids, then dst
-  int base[kMaxE], Pe[kMaxE], slot[kMaxE];
-  int keep[kMaxR], segA[kMaxR], segB[kMaxR], recv[kMaxR], rfirst[kMaxR], rcnt[kMaxR];
+  int T[kMaxE];     // routes of expert e over all source ranks
+  int base[kMaxE];  // routes of e in tiles before this one
+  int Pe[kMaxE];    // start of e in its home rank's stream
+  int hst[kMaxE];   // start row of home group e on its owner
+  int sst[kMaxE];   // [u*Eg + j]: start row of the slot group of receiver u that
+                    // holds its donor's j-th expert, -1 if none
+  int Lh[kMaxR], keep[kMaxR], donor[kMaxR], segA[kMaxR], segB[kMaxR];
+  int recv[kMaxR], rfirst[kMaxR], rcnt[kMaxR];
+  int wflags[kPlanWaves];
   int wc[kPlanWaves * kMaxR * 2];          // per-wave duplicate groups / rows per rank
   int baseD[kMaxR * 2], tot[kMaxR * 2];
-  int cu[kCuLds];
   int flags;
 };
 
-template <bool kCuInLds>
-__device__ __forceinline__ int cu_at(const PlaceLds& L, const int32_t* __restrict__ cu, int i) {
-  return kCuInLds ? L.cu[i] : cu[i];
-}
+// Status bits that leave the plan without a layout: every tile finds them
+// from the same data, so all tiles stop together.
+constexpr int kFatal = kBadExpert | kSlotBudget | kInternal;
 
 // Duplicate groups and rows of tile-group word w for rank field x.
 __device__ __forceinline__ int word_field(uint64_t w, int f) {
   return f == 0 ? (int)((w >> 24) & 0xFFFFFFu) : (int)(w & 0xFFFFFFu);
 }
 
-template <bool kCuInLds>
-__device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, const Scratch& sc,
-                           const PlanArrays& pa, PlaceLds& L, uint32_t tag) {
+// Tile counts of a batch of experts e0, e0 + 16, ..: lane l holds tiles
+// 4l..4l+3 (one 16-byte load).  Expert e = w + 16i is checked against the
+// given histogram by wave w of the tiles t = i mod tiles (bit i of `chk`);
+// there lanes r < R also fetch tokens_per_expert[r][e].
+__device__ __forceinline__ void load_count_batch(const Dims& d, const Scratch& sc,
+                                                 const int32_t* __restrict__ tpe, uint32_t chk,
+                                                 int e0, int (&c)[kScanBatch][kTilesPerLane],
+                                                 int (&given)[kScanBatch]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int j = 0; j < kScanBatch; ++j) {
+    const int e = e0 + j * kPlanWaves;
+    int4 v = {0, 0, 0, 0};
+    if (e < d.E && lane * 4 < d.ntiles)
+      v = *reinterpret_cast<const int4*>(sc.tile_cnt + e * d.ntiles_pad + lane * 4);
+    c[j][0] = v.x;
+    c[j][1] = v.y;
+    c[j][2] = v.z;
+    c[j][3] = v.w;
+    given[j] = (e < d.E && ((chk >> (e / kPlanWaves)) & 1u) && lane < d.R) ? tpe[lane * d.E + e] : 0;
+  }
+}
+
+// Expert totals and this tile's bases from a loaded batch; the checking tile
+// compares each rank's count of e (a rank's tiles are consecutive) with the
+// given histogram.  Returns status bits found.
+__device__ __forceinline__ int reduce_count_batch(const Dims& d, PlanLds& L, uint32_t chk,
+                                                  int e0, int t,
+                                                  const int (&c)[kScanBatch][kTilesPerLane],
+                                                  const int (&given)[kScanBatch]) {
+  const int lane = lane_id();
+  const int tl = t >> 2, sub_t = t & 3;
+  int bits = 0;
+#pragma unroll
+  for (int j = 0; j < kScanBatch; ++j) {
+    const int e = e0 + j * kPlanWaves;
+    if (e >= d.E) break;
+    const int sum4 = c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    const int incl = wave_incl_scan(sum4);
+    const int ex0 = incl - sum4;  // routes of e in tiles before 4*lane
+    const int part = (sub_t > 0 ? c[j][0] : 0) + (sub_t > 1 ? c[j][1] : 0) +
+                     (sub_t > 2 ? c[j][2] : 0);
+    const int bse = __builtin_amdgcn_readlane(ex0 + part, tl);
+    const int total = lane63(incl);
+    if (lane == 0) {
+      L.T[e] = total;
+      L.base[e] = bse;
+    }
+    if ((chk >> (e / kPlanWaves)) & 1u) {
+      // Lane x <= R fetches the prefix at tile x * tiles_per_rank.
+      const int tile = min(lane, d.R) * d.tiles_per_rank;
+      const int src = min(tile / kTilesPerLane, kWave - 1), sub = tile % kTilesPerLane;
+      const int v0 = __shfl(ex0, src, kWave);
+      const int v1 = __shfl(ex0 + c[j][0], src, kWave);
+      const int v2 = __shfl(ex0 + c[j][0] + c[j][1], src, kWave);
+      const int v3 = __shfl(ex0 + c[j][0] + c[j][1] + c[j][2], src, kWave);
+      int pre = sub == 0 ? v0 : sub == 1 ? v1 : sub == 2 ? v2 : v3;
+      if (tile >= d.ntiles) pre = total;
+      const int next = __shfl_down(pre, 1, kWave);
+      if (__ballot(lane < d.R && next - pre != given[j])) bits |= kHistogram;
+    }
+  }
+  return bits;
+}
+
+// The alias fill (one wave, lane = rank).  Under-loaded ranks, in ascending
+// order, take what they lack from the lowest over-loaded rank; a donor pushed
+// below S*K joins the back of the receiver queue.  Donors are used up in
+// ascending order, so the appended receivers come after all initial ones and
+// in ascending order too: both queues are bit masks.
+__device__ __forceinline__ void alias_fill(const Dims& d, PlanLds& L) {
+  const int lane = lane_id();
+  const int R = d.R;
+  const int C = d.S * d.K;
+  int rem = lane < R ? L.Lh[lane] : C;
+  int donor = -1, take = 0, off = 0, given = 0;
+  int recv = 0, rfirst = 0, rcnt = 0;  // lane j: j-th receiver served; lane o: donor o's range
+  uint64_t small = __ballot(rem < C), large = __ballot(rem > C), appended = 0;
+  int served = 0;
+  bool broken = false;
+  while (small | appended) {
+    int u;
+    if (small) {
+      u = __ffsll((unsigned long long)small) - 1;
+      small &= small - 1;
+    } else {
+      u = __ffsll((unsigned long long)appended) - 1;
+      appended &= appended - 1;
+    }
+    if (!large) {  // cannot happen: the loads sum to R*C
+      broken = true;
+      break;
+    }
+    const int o = __ffsll((unsigned long long)large) - 1;
+    // u and o are uniform (taken from ballot masks): read their lanes directly
+    const int f = C - __builtin_amdgcn_readlane(rem, u);
+    const int g_o = __builtin_amdgcn_readlane(given, o);
+    const int rem_o = __builtin_amdgcn_readlane(rem, o) - f;
+    const int cnt_o = __builtin_amdgcn_readlane(rcnt, o);
+    if (lane == u) {
+      donor = o;
+      take = f;
+      off = g_o;
+    }
+    if (lane == o) {
+      given = g_o + f;
+      rem = rem_o;
+      if (cnt_o == 0) rfirst = served;
+      rcnt = cnt_o + 1;
+    }
+    if (lane == served) recv = u;
+    ++served;
+    if (rem_o < C) {
+      large &= large - 1;
+      appended |= 1ull << o;
+    } else if (rem_o == C) {
+      large &= large - 1;
+    }
+  }
+  if (broken && lane == 0) atomicOr(&L.flags, kInternal);
+  const int keep = rem;
+  const int dk = __shfl(keep, donor < 0 ? 0 : donor, kWave);
+  if (lane < R) {
+    L.keep[lane] = keep;
+    L.donor[lane] = donor;
+    L.segA[lane] = donor >= 0 ? dk + off : 0;
+    L.segB[lane] = donor >= 0 ? dk + off + take : 0;
+    L.recv[lane] = recv;
+    L.rfirst[lane] = rfirst;
+    L.rcnt[lane] = rcnt;
+  }
+}
+
+// Rank u's padded groups (one wave): its home experts u*Eg.. in ascending id,
+// then its slots (the donor's experts overlapping its segment, ascending id,
+// from slot 0).  Every other expert group of u is empty.  Start rows go to
+// LDS; when `writer`, the rank's plan arrays are written as well.
+__device__ __forceinline__ void rank_layout(const Dims& d, const PlanArrays& pa, PlanLds& L, int u,
+                                            bool writer) {
+  const int lane = lane_id();
+  const int E = d.E, Eg = d.Eg, B = d.B, EB = d.EB, P = d.P;
+  int32_t* cu = pa.cu + u * EB;
+  int32_t* zfr = pa.zfr + u * EB * 2;
+  int carry = 0;
+  for (int j0 = 0; j0 < Eg; j0 += kWave) {
+    const int j = j0 + lane, g = u * Eg + j;
+    int n = 0;
+    if (j < Eg) n = min(max(L.keep[u] - L.Pe[g], 0), L.T[g]);
+    const int pad = n == 0 ? 0 : (n + P - 1) / P * P;
+    const int incl = wave_incl_scan(pad);
+    if (j < Eg) {
+      const int end = carry + incl;
+      L.hst[g] = end - pad;
+      if (writer) {
+        cu[g] = end;
+        zfr[g * 2 + 0] = end - pad + n;
+        zfr[g * 2 + 1] = end;
+      }
+    }
+    carry += lane63(incl);
+  }
+  if (writer) {
+    for (int g = lane; g < E; g += kWave) {
+      if (g / Eg == u) continue;
+      const int end = g < u * Eg ? 0 : carry;
+      cu[g] = end;
+      zfr[g * 2 + 0] = end;
+      zfr[g * 2 + 1] = end;
+    }
+  }
+  const int o = L.donor[u];
+  int count = 0, routed = 0, bits = 0;
+  for (int j0 = 0; j0 < Eg; j0 += kWave) {
+    const int j = j0 + lane;
+    bool piece = false;
+    int len = 0;
+    if (o >= 0 && j < Eg) {
+      const int e = o * Eg + j;
+      const int lo = max(L.Pe[e], L.segA[u]);
+      const int hi = min(L.Pe[e] + L.T[e], L.segB[u]);
+      piece = L.T[e] > 0 && lo < hi;
+      len = hi - lo;
+    }
+    const uint64_t m = __ballot(piece);
+    const int slot = count + __popcll(m & lanes_below());
+    const bool kept = piece && slot < B;
+    const int n = kept ? len : 0;
+    const int pad = n == 0 ? 0 : (n + P - 1) / P * P;
+    const int incl = wave_incl_scan(pad);
+    const int end = carry + incl;
+    if (j < Eg) L.sst[u * Eg + j] = kept ? end - pad : -1;
+    if (writer && kept) {
+      pa.etc[u * B + slot] = o * Eg + j;
+      cu[E + slot] = end;
+      zfr[(E + slot) * 2 + 0] = end - pad + n;
+      zfr[(E + slot) * 2 + 1] = end;
+    }
+    if (__ballot(piece && !kept)) bits |= kSlotBudget;
+    routed += n;
+    count += __popcll(m);
+    carry += lane63(incl);
+  }
+  if (bits && lane == 0) atomicOr(&L.flags, bits);
+  if (writer) {
+    routed = wave_sum(routed);
+    const int used = min(count, B);
+    for (int j = used + lane; j < B; j += kWave) {
+      pa.etc[u * B + j] = -1;
+      cu[E + j] = carry;
+      zfr[(E + j) * 2 + 0] = carry;
+      zfr[(E + j) * 2 + 1] = carry;
+    }
+    if (lane == 0) {
+      pa.rstats[u * 2 + 0] = used;
+      pa.rstats[u * 2 + 1] = routed;
+    }
+  }
+}
+
+// Publish zero duplicate counts for tile t (so that no later tile waits on
+// it) and report the tile's status bits.
+__device__ __forceinline__ void stop_tile(const Dims& d, const Scratch& sc, const PlanArrays& pa,
+                                          uint32_t tag, int flags) {
+  for (int u = threadIdx.x; u < d.R; u += kPlanThreads)
+    __hip_atomic_store(sc.tile_agg + blockIdx.x * d.R + u, pack_word(tag, 0, 0), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0 && flags != 0) atomicOr(&pa.status[0], flags);
+}
+
+__device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk,
+                           const int32_t* __restrict__ tpe, const Scratch& sc,
+                           const PlanArrays& pa, PlanLds& L, uint32_t tag) {
   const int lane = lane_id(), wave = wave_id();
-  const int E = d.E, R = d.R, K = d.K, Eg = d.Eg, EB = d.EB, NvS = d.NvS, nt = d.ntiles;
+  const int E = d.E, R = d.R, K = d.K, Eg = d.Eg, NvS = d.NvS, nt = d.ntiles;
   const int t = blockIdx.x;
   const TileRange tr = tile_range(d, t);
   int ws0, ws1;
@@ -445,84 +450,95 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, cons
   int* wc = L.wc + wave * R * 2;
   const bool staged = nchunks <= kBatch;
 
-  // ---- Tables and this wave's first batch of routes, all loads in flight together.
+  // ---- This wave's first batch of routes, the first batch of its experts'
+  // tile counts and (wave 0) the out-of-range flags of all tiles: all loads
+  // in flight together.
+  int tc[kScanBatch][kTilesPerLane], given[kScanBatch];
+  int wbits = 0;
+  // Groups of 16 experts this tile checks against the given histogram.
+  uint32_t chk = 0;
+  if (tpe != nullptr)
+    for (int i = t; i < kMaxE / kPlanWaves; i += nt) chk |= 1u << i;
   {
     int v[kBatch];
 #pragma unroll
-    for (int c = 0; c < kBatch; ++c) {
-      const int tok = ws0 + c * ctok;
-      const int nl = (c < nchunks) ? min(ctok, ws1 - tok) * K : 0;
-      v[c] = lane < nl ? topk[(rowbase + tok) * K + lane] : -1;
+    for (int cc = 0; cc < kBatch; ++cc) {
+      const int tok = ws0 + cc * ctok;
+      const int nl = (cc < nchunks) ? min(ctok, ws1 - tok) * K : 0;
+      v[cc] = lane < nl ? topk[(rowbase + tok) * K + lane] : -1;
     }
-    // Every table element this thread stages (E <= kMaxE <= kPlanThreads, so
-    // one per expert array; R*EB <= kCuLds) is loaded before any is stored,
-    // so the loads share one memory round trip.
-    const int me = threadIdx.x;
-    const bool xe = me < E, xr = me < R;
-    const int pe = xe ? sc.Pe[me] : 0;
-    const int so = xe ? sc.slot_of[me] : 0;
-    const int bs = xe ? sc.base[me * nt + t] : 0;
-    int cuv[kCuLds / kPlanThreads];
+    load_count_batch(d, sc, tpe, chk, wave, tc, given);
+    int4 bad = {0, 0, 0, 0};
+    if (wave == 0 && lane * 4 < nt)
+      bad = *reinterpret_cast<const int4*>(sc.tile_cnt + E * d.ntiles_pad + lane * 4);
+    // The wave's own LDS regions: no other wave touches them before the
+    // next barrier.
+    for (int x = lane; x < E; x += kWave) run[x] = 0;
+    for (int x = lane; x < R * 2; x += kWave) wc[x] = 0;
 #pragma unroll
-    for (int i = 0; i < kCuLds / kPlanThreads; ++i) {
-      const int j = me + i * kPlanThreads;
-      cuv[i] = (kCuInLds && j < R * EB) ? pa.cu[j] : 0;
-    }
-    int kp = 0, sa = 0, sb = 0, rv = 0, rf = 0, rc = 0;
-    if (xr) {
-      kp = sc.keep[me];
-      sa = sc.seg_a[me];
-      sb = sc.seg_b[me];
-      rv = sc.recv[me];
-      rf = sc.recv_first[me];
-      rc = sc.recv_cnt[me];
-    }
-    if (xe) {
-      L.Pe[me] = pe;
-      L.slot[me] = so;
-      L.base[me] = bs;
-    }
-#pragma unroll
-    for (int i = 0; i < kCuLds / kPlanThreads; ++i) {
-      const int j = me + i * kPlanThreads;
-      if (kCuInLds && j < R * EB) L.cu[j] = cuv[i];
-    }
-    if (xr) {
-      L.keep[me] = kp;
-      L.segA[me] = sa;
-      L.segB[me] = sb;
-      L.recv[me] = rv;
-      L.rfirst[me] = rf;
-      L.rcnt[me] = rc;
-    }
-    for (int x = threadIdx.x; x < kPlanWaves * E; x += kPlanThreads) L.run[x] = 0;
-    for (int x = threadIdx.x; x < kPlanWaves * R * 2; x += kPlanThreads) L.wc[x] = 0;
-    if (threadIdx.x == 0) L.flags = 0;
-#pragma unroll
-    for (int c = 0; c < kBatch; ++c) st[c * kWave + lane] = v[c];
+    for (int cc = 0; cc < kBatch; ++cc) st[cc * kWave + lane] = v[cc];
+    if (__ballot((bad.x | bad.y | bad.z | bad.w) != 0)) wbits |= kBadExpert;
   }
-  __syncthreads();
-  // Per-wave expert counts of the tile (recounted from the routes), then
-  // running positions = tile base + counts of earlier waves.
-  for (int c = 0; c < nchunks; ++c) {
-    const int tok = ws0 + c * ctok;
+  // Per-wave expert counts of the tile (recounted from the routes).
+  wave_lds_fence();
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const int tok = ws0 + cc * ctok;
     const int nl = min(ctok, ws1 - tok) * K;
     if (lane < nl) {
-      const int e = staged ? st[c * kWave + lane] : topk[(rowbase + tok) * K + lane];
-      atomicAdd(&run[e], 1);
+      const int e = staged ? st[cc * kWave + lane] : topk[(rowbase + tok) * K + lane];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&run[e], 1);
     }
   }
+  // Expert totals and this tile's bases.
+  for (int e0 = wave; e0 < E; e0 += kScanBatch * kPlanWaves) {
+    if (e0 != wave) load_count_batch(d, sc, tpe, chk, e0, tc, given);
+    wbits |= reduce_count_batch(d, L, chk, e0, t, tc, given);
+  }
+  if (lane == 0) L.wflags[wave] = wbits;
   __syncthreads();
+
+  // ---- Running positions = tile base + counts of earlier waves; home stream
+  // offsets (home rank h's stream is its experts in ascending id).
+  if (threadIdx.x == 0) {
+    int f = 0;
+    for (int w = 0; w < kPlanWaves; ++w) f |= L.wflags[w];
+    L.flags = f;
+  }
   for (int e = threadIdx.x; e < E; e += kPlanThreads) {
     int acc = L.base[e];
 #pragma unroll
     for (int w = 0; w < kPlanWaves; ++w) {
-      const int c = L.run[w * E + e];
+      const int cnt = L.run[w * E + e];
       L.run[w * E + e] = acc;
-      acc += c;
+      acc += cnt;
     }
   }
+  for (int h = wave; h < R; h += kPlanWaves) {
+    int carry = 0;
+    for (int j0 = 0; j0 < Eg; j0 += kWave) {
+      const int j = j0 + lane;
+      const int v = j < Eg ? L.T[h * Eg + j] : 0;
+      const int incl = wave_incl_scan(v);
+      if (j < Eg) L.Pe[h * Eg + j] = carry + incl - v;
+      carry += lane63(incl);
+    }
+    if (lane == 0) L.Lh[h] = carry;
+  }
   __syncthreads();
+  if (L.flags & kBadExpert) {
+    stop_tile(d, sc, pa, tag, L.flags);
+    return;
+  }
+
+  // ---- Balance and layout.
+  if (wave == 0) alias_fill(d, L);
+  __syncthreads();
+  for (int u = wave; u < R; u += kPlanWaves) rank_layout(d, pa, L, u, t == u);
+  __syncthreads();
+  if (L.flags & kFatal) {
+    stop_tile(d, sc, pa, tag, L.flags);
+    return;
+  }
 
   // ---- Placement.
   for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
@@ -549,10 +565,10 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, cons
         const int pos = run[e] + rank;  // position among e's routes
         const int h = e / Eg;
         const int q = L.Pe[e] + pos;    // position in h's stream
-        int g, idx;
+        int start, idx;
         if (q < L.keep[h]) {
           u = h;
-          g = e;
+          start = L.hst[e];
           idx = q - L.Pe[e];
         } else {
           const int f0 = L.rfirst[h], nr = L.rcnt[h];
@@ -563,18 +579,17 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, cons
               break;
             }
           }
-          const int slot = u >= 0 ? L.slot[u * Eg + (e - h * Eg)] : -1;
-          if (u < 0 || slot < 0) {  // cannot happen for a consistent plan
+          const int s0 = u >= 0 ? L.sst[u * Eg + (e - h * Eg)] : -1;
+          if (s0 < 0) {  // cannot happen for a consistent plan
             atomicOr(&L.flags, kInternal);
             u = 0;
-            g = 0;
+            start = 0;
             idx = 0;
           } else {
-            g = E + slot;
+            start = s0;
             idx = q - max(L.Pe[e], L.segA[u]);
           }
         }
-        const int start = g == 0 ? 0 : cu_at<kCuInLds>(L, pa.cu, u * EB + g - 1);
         G = u * NvS + start + idx;
       }
       wave_lds_fence();
@@ -657,10 +672,8 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, cons
   }
   if (timeout) atomicOr(&L.flags, kInternal);
   __syncthreads();
-  if (L.flags != 0) {
-    if (threadIdx.x == 0) atomicOr(&pa.status[0], L.flags);
-    return;
-  }
+  if (threadIdx.x == 0 && L.flags != 0) atomicOr(&pa.status[0], L.flags);
+  if (L.flags & kFatal) return;
   for (int x = threadIdx.x; x < kPlanWaves * R * 2; x += kPlanThreads)
     L.wc[x] += L.baseD[x % (R * 2)];
   if (t == nt - 1)
@@ -713,27 +726,18 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk, cons
 }
 
 __global__ void __launch_bounds__(kPlanThreads)
-    k_plan_place(Dims d, const int32_t* __restrict__ topk, Scratch sc, PlanArrays pa) {
-  __shared__ PlaceLds L;
-  const uint32_t tag = sc.epoch[0];
-  if (pa.status[0] != 0) {
-    // Nothing to place; still publish, so that no later tile waits on this one.
-    for (int u = threadIdx.x; u < d.R; u += kPlanThreads)
-      __hip_atomic_store(sc.tile_agg + blockIdx.x * d.R + u, pack_word(tag, 0, 0),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
-  if (d.R * d.EB <= kCuLds) place_tile<true>(d, topk, sc, pa, L, tag);
-  else place_tile<false>(d, topk, sc, pa, L, tag);
+    k_plan_place(Dims d, const int32_t* __restrict__ topk, const int32_t* __restrict__ tpe,
+                 Scratch sc, PlanArrays pa) {
+  __shared__ PlanLds L;
+  place_tile(d, topk, tpe, sc, pa, L, sc.epoch[0]);
 }
 
 }  // namespace
 
 hipError_t launch_plan(const Dims& d, const Scratch& sc, const PlanArrays& pa, const int32_t* topk,
                        const int32_t* tpe, hipStream_t s) {
-  hipLaunchKernelGGL(k_plan_count, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, topk, sc);
-  hipLaunchKernelGGL(k_plan_balance, dim3(1), dim3(kPlanThreads), 0, s, d, tpe, sc, pa);
-  hipLaunchKernelGGL(k_plan_place, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, topk, sc, pa);
+  hipLaunchKernelGGL(k_plan_count, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, topk, sc, pa);
+  hipLaunchKernelGGL(k_plan_place, dim3(d.ntiles), dim3(kPlanThreads), 0, s, d, topk, tpe, sc, pa);
   return hipGetLastError();
 }
 
