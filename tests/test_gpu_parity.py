@@ -143,6 +143,7 @@ EDGE = [
     ("k64", 2, 8, 64, 9, 8, 0, 4, "repeats"),
     ("b-small-ok", 4, 16, 2, 64, 16, 1, 4, "uniform"),
     ("large-e", 8, 512, 8, 128, 16, 0, 8, "skewed"),
+    ("max-tiles-e512", 32, 512, 8, 1024, 16, 0, 4, "skewed"),  # 256 planner tiles
 ]
 
 
@@ -278,6 +279,45 @@ def test_device_status_and_skip(env, what):
         assert oracle.plan(topk, E, B, P, tokens_per_expert=tpe).status == \
             {moon.MOON_OK: 0, moon.MOON_ERR_BAD_EXPERT: -7, moon.MOON_ERR_HISTOGRAM: -9,
              moon.MOON_ERR_SLOT_BUDGET: -8, moon.MOON_ERR_NOT_PLANNED: 0}[expect]
+    finally:
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
+
+
+@pytest.mark.parametrize("R,E,K,S", [(32, 512, 8, 1024), (8, 256, 8, 256), (3, 12, 3, 1000)],
+                         ids=["256-tiles", "16-tiles", "ragged"])
+def test_histogram_check_every_expert(env, R, E, K, S):
+    """tokens_per_expert is checked for every (rank, expert): a plan with the
+    true histogram equals the oracle's; moving one route's count between two
+    experts of one rank, anywhere in the matrix, gives HISTOGRAM."""
+    import torch
+    moon, dev = env
+    rng = np.random.default_rng(zlib.crc32(f"hist-{R}-{E}".encode()))
+    topk = _edge_topk(rng, R, S, K, E, "skewed")
+    tpe = np.stack([np.bincount(topk[r].reshape(-1), minlength=E) for r in range(R)]).astype(
+        np.int32)
+    H, P = 16, 4
+    hidden = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * S * H).reshape(R, S, H)
+    nvs = oracle.nvs(R, E, K, S, E // R, P)
+    y = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * nvs * H).reshape(R * nvs, H)
+    run_full(moon, dev, topk, None, hidden, y, R, E, K, S, H, 0, P, weighted=False,
+             label=f"histogram given R={R} E={E}", tpe=tpe)
+    ctx = moon.moon_ctx_create(R, E, K, S, H, 0, P)
+    plan = moon.moon_plan_create(ctx)
+    try:
+        topk_d = pt.to_dev(topk, dev)
+        spots = sorted({(r, e) for r in (0, R // 2, R - 1)
+                        for e in (0, 15, 16, 17, E // 2, E - 17, E - 1) if 0 <= e < E})
+        say(f"[case] histogram perturbations R={R} E={E}: {len(spots)}")
+        for r, e in spots:
+            bad = tpe.copy()
+            bad[r, e] += 1
+            bad[r, (e + 1) % E] -= 1
+            moon.moon_plan(ctx, topk_d, pt.to_dev(bad, dev), plan)
+            st = moon.moon_plan_status(plan)
+            assert st == moon.MOON_ERR_HISTOGRAM, (r, e, moon.moon_status_str(st))
+        moon.moon_plan(ctx, topk_d, pt.to_dev(tpe, dev), plan)
+        assert moon.moon_plan_status(plan) == moon.MOON_OK
     finally:
         moon.moon_plan_destroy(plan)
         moon.moon_ctx_destroy(ctx)
