@@ -69,17 +69,6 @@ __device__ __forceinline__ int lane63(int v) { return __builtin_amdgcn_readlane(
 
 __device__ __forceinline__ int wave_sum(int v) { return lane63(wave_incl_scan(v)); }
 
-// Lanes of `set` whose `key` equals this lane's key (ballot over key bits).
-__device__ __forceinline__ uint64_t match_key(uint64_t set, int key, int bits) {
-  uint64_t peers = set;
-  for (int b = 0; b < bits; ++b) {
-    const bool bit = (key >> b) & 1;
-    const uint64_t m = __ballot(bit);
-    peers &= bit ? m : ~m;
-  }
-  return peers;
-}
-
 __device__ __forceinline__ uint64_t get_word(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
