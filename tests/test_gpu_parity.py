@@ -228,6 +228,62 @@ def test_clone_repeat_and_backward_reuse(env):
         moon.moon_ctx_destroy(ctx)
 
 
+def test_two_contexts_on_two_streams(env):
+    """Contexts are independent: two of them, each planning, dispatching and
+    combining on its own stream (default priority) at the same time, give the
+    oracle's results, call after call."""
+    import torch
+    moon, dev = env
+    shapes = [(4, 32, 4, 300, 64, 0, 4), (8, 64, 6, 160, 32, 0, 16)]
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    runs = []
+    for n, (R, E, K, S, H, B, P) in enumerate(shapes):
+        rng = np.random.default_rng(900 + n)
+        ins = []
+        for rep in range(2):
+            topk = _edge_topk(rng, R, S, K, E, "skewed" if rep else "uniform")
+            w = rng.random((R, S, K)).astype(np.float32)
+            hidden = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * S * H).reshape(R, S, H)
+            ins.append((topk, w, hidden))
+        ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+        y = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * ctx.NvS * H).reshape(
+            R * ctx.NvS, H)
+        runs.append(dict(ctx=ctx, plan=moon.moon_plan_create(ctx), ins=ins, y=y,
+                         dev=[(pt.to_dev(t, dev), pt.to_dev(w, dev), pt.bf16_to_dev(h, dev))
+                              for t, w, h in ins],
+                         y_d=pt.bf16_to_dev(y, dev),
+                         out=torch.empty((R, S, H), dtype=torch.bfloat16, device=dev),
+                         shape=(R, E, K, S, H, B, P)))
+    torch.cuda.synchronize()
+    say("[case] two contexts on two streams")
+    try:
+        for it in range(6):
+            for n, r in enumerate(runs):  # issue both before waiting on either
+                t_d, w_d, h_d = r["dev"][it % 2]
+                st = streams[n]
+                moon.moon_plan(r["ctx"], t_d, None, r["plan"], stream=st)
+                moon.moon_dispatch(r["ctx"], r["plan"], h_d, w_d, stream=st)
+                _, wwin = moon.window_tensors(r["ctx"])
+                moon.moon_combine(r["ctx"], r["plan"], r["y_d"], wwin, moon.MOON_COMBINE_WEIGHTED,
+                                  r["out"], stream=st)
+            for n, r in enumerate(runs):
+                R, E, K, S, H, B, P = r["shape"]
+                assert moon.moon_plan_status(r["plan"], streams[n]) == moon.MOON_OK
+                topk, w, hidden = r["ins"][it % 2]
+                ref = oracle.plan(topk, E, r["ctx"].B, P)
+                pt.compare_plan(pt.gpu_plan_arrays(r["plan"]), ref)
+                win, wwin = moon.window_tensors(r["ctx"])
+                ewin, ewwin = oracle.dispatch(ref, hidden, w)
+                cov = oracle.row_sources(ref) != -2
+                assert np.array_equal(pt.dev_bits(win)[cov], ewin[cov]), (it, n)
+                eout, _, _ = oracle.combine(ref, r["y"], ewwin, weighted=True)
+                assert np.array_equal(pt.dev_bits(r["out"]), eout), (it, n)
+    finally:
+        for r in runs:
+            moon.moon_plan_destroy(r["plan"])
+            moon.moon_ctx_destroy(r["ctx"])
+
+
 @pytest.mark.parametrize("what", ["bad_high", "bad_negative", "histogram", "slot_budget",
                                   "not_planned", "tpe_ok"])
 def test_device_status_and_skip(env, what):
