@@ -17,8 +17,10 @@
 //                       scatters the K route weights.  Further items zero the
 //                       padding rows of every (rank, group), eight rows each.
 //   k_dispatch_expand   persistent grid; a work item is one wave on a 4 KB
-//                       slice of one duplicate group's primary row; the lanes
-//                       also fetch the group's duplicate row offsets, then the
+//                       slice of one duplicate group's primary row (plain
+//                       loads where the scatter kept the primaries in the
+//                       caches, non-temporal ones otherwise); the lanes also
+//                       fetch the group's duplicate row offsets, then the
 //                       slice is stored to each duplicate row.
 //
 // All copies move bits; no floating-point arithmetic is done.
@@ -33,7 +35,6 @@ constexpr int kSliceVec = 2;       // 16-byte vectors per lane in a scatter slic
 constexpr int kZeroRows = 8;       // padding rows per zero-fill item
 constexpr int kScatterBlocks = 32768;  // persistent grids (a sweep of 2048, 8192, 32768)
 constexpr int kExpandBlocks = 32768;
-constexpr bool kScatterNtLoad = false;  // non-temporal: -1.8 % at r8-e64-k6, +1.6 % at DSv3
 // Half of the 256 MB last-level cache (MI355X): the largest token-row size
 // R*S*2H of a call for which the scatter caches the re-read primaries.
 constexpr int64_t kKeepBudgetBytes = 128ll << 20;
@@ -70,7 +71,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int c = 0; c < kSliceVec; ++c) {
         const int j = c0 + c * kWave + lane;
-        if (j < V) buf[c] = kScatterNtLoad ? __builtin_nontemporal_load(src + j) : src[j];
+        if (j < V) buf[c] = src[j];  // (non-temporal loads: 1 % slower at DSv3 and R=16)
       }
       if (status != 0) return;
       if (wlane) wwin[dst_global_row(dl)] = wk;
@@ -127,8 +128,10 @@ __global__ void __launch_bounds__(kThreads)
 
 // Work item = (duplicate group, slice of SW = 64*SV vectors).  A wave takes UI
 // items at once: it loads their records, then their primary slices and (one
-// lane per duplicate) their duplicate row offsets, then stores.
-template <int SV, int UI>
+// lane per duplicate) their duplicate row offsets, then stores.  NTL: read
+// the primaries with non-temporal loads (when the scatter did not keep them
+// in the caches).
+template <int SV, int UI, bool NTL>
 __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays pa,
                                                               u32x4* __restrict__ win) {
   constexpr int SW = kWave * SV;
@@ -173,7 +176,7 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays
 #pragma unroll
       for (int cc = 0; cc < SV; ++cc) {
         const int j = j0[i] + cc * kWave;
-        if (m[i] > 0 && j < V) buf[i][cc] = sp[j];
+        if (m[i] > 0 && j < V) buf[i][cc] = NTL ? __builtin_nontemporal_load(sp + j) : sp[j];
       }
     }
 #pragma unroll
@@ -217,8 +220,15 @@ hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* 
   const int64_t ewant = (bound + kWavesPerBlock * kExpandUnroll - 1) /
                         (kWavesPerBlock * kExpandUnroll);
   const int eblocks = (int)(ewant < kExpandBlocks ? (ewant > 0 ? ewant : 1) : kExpandBlocks);
-  hipLaunchKernelGGL((k_dispatch_expand<kExpandSliceVec, kExpandUnroll>), dim3(eblocks),
-                     dim3(kThreads), 0, s, d, pa, reinterpret_cast<u32x4*>(win));
+  // Primaries the scatter kept in the caches are read with plain loads, the
+  // others with non-temporal ones (2.4 % of dispatch at the DSv3 shape; 5 %
+  // slower where the primaries are kept).
+  if (keep)
+    hipLaunchKernelGGL((k_dispatch_expand<kExpandSliceVec, kExpandUnroll, false>), dim3(eblocks),
+                       dim3(kThreads), 0, s, d, pa, reinterpret_cast<u32x4*>(win));
+  else
+    hipLaunchKernelGGL((k_dispatch_expand<kExpandSliceVec, kExpandUnroll, true>), dim3(eblocks),
+                       dim3(kThreads), 0, s, d, pa, reinterpret_cast<u32x4*>(win));
   return hipGetLastError();
 }
 
