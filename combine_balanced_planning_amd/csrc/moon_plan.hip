@@ -626,7 +626,10 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk,
 
   // ---- Counts of earlier tiles: for each rank, lane l reads tiles l,
   // l+64, .. below this one (one packed word each, all in flight together).
-  // Every wait is on a lower tile, which publishes before it waits.
+  // Every wait is on a lower tile, which publishes before it waits; the
+  // hardware starts workgroups in index order, so a lower tile is already
+  // running or done when a higher one waits for it, even when other kernels
+  // share the device.
   bool timeout = false;
   const uint32_t tag16 = tag & 0xFFFFu;
   for (int u = wave; u < R; u += kPlanWaves) {
