@@ -1,0 +1,125 @@
+"""bench.py's host-side contract, without a GPU: it refuses more than one GPU,
+its source hashes ignore comments (they decide whether recorded counter
+readings still apply), and its rocprofv3 summarizers turn counter and trace
+CSV folders into the figures the bench line reports."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_code_hash_ignores_comments_not_code():
+    c = "int f(int x) {\n  // twice\n  return 2 * x; /* doubled */\n}\n"
+    c_comment = "int f(int x) {\n  // two times x\n  return 2 * x;   /* x + x */\n}\n"
+    c_code = "int f(int x) {\n  // twice\n  return 3 * x; /* doubled */\n}\n"
+    assert bench._code_only(c, "a.hip") == bench._code_only(c_comment, "a.hip")
+    assert bench._code_only(c, "a.hip") != bench._code_only(c_code, "a.hip")
+    p = "def f(x):\n    # twice\n    return 2 * x\n"
+    assert bench._code_only(p, "a.py") == bench._code_only(p.replace("twice", "doubled"), "a.py")
+    assert bench._code_only(p, "a.py") != bench._code_only(p.replace("2 *", "3 *"), "a.py")
+
+
+def test_kernel_sources_follow_the_kernel_file():
+    assert bench.kernel_sources("k_combine<false, 1, 2>")[-1].endswith("moon_combine.hip")
+    assert bench.kernel_sources("k_dispatch_expand<4, 1, true>")[-1].endswith("moon_dispatch.hip")
+    assert bench.kernel_sources("k_plan_place")[-1].endswith("moon_plan.hip")
+    for k in ("k_combine", "k_plan_count"):
+        assert set(bench.PMC_COMMON) <= set(bench.kernel_sources(k))
+
+
+def _write_csv(path, fields, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def _counters(path, launches):
+    """launches: [(full kernel name, KiB)]"""
+    _write_csv(path, ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               [{"Kernel_Name": n, "Counter_Name": "X", "Counter_Value": v} for n, v in launches])
+
+
+K_COMBINE = "void moon::(anonymous namespace)::k_combine<false, 1, 2>(moon::Dims, ...)"
+K_EXPAND = "void moon::(anonymous namespace)::k_dispatch_expand<4, 1, true>(moon::Dims, ...)"
+COPY = "void at::native::vectorized_elementwise_kernel<4>(int, ...)"
+
+
+def test_pmc_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(bench.PROFILES)
+    d = tmp_path / "raw"
+    # step runs: two combine launches, three expand launches of another
+    # instantiation (the most-launched instantiation is the one reported)
+    _counters(str(d / "f" / "run_counter_collection.csv"),
+              [(K_COMBINE, 1000.0), (K_COMBINE, 1200.0)] + [(K_EXPAND, 300.0)] * 3 +
+              [(COPY, 5.0)])
+    _counters(str(d / "w" / "run_counter_collection.csv"),
+              [(K_COMBINE, 500.0), (K_COMBINE, 500.0)] + [(K_EXPAND, 100.0)] * 3 +
+              [(COPY, 5.0)])
+    # calibration: a 1 GiB copy read as 0.5 GiB by the fetch counter, 1 GiB written
+    gib_kib = (1 << 30) / 1024.0
+    _counters(str(d / "cf" / "run_counter_collection.csv"), [(COPY, gib_kib / 2)] * 5)
+    _counters(str(d / "cw" / "run_counter_collection.csv"), [(COPY, gib_kib)] * 5)
+    bench.summarize_pmc("wl-test", [str(d / x) for x in ("f", "w", "cf", "cw")], ["cmd"])
+    rec = json.load(open(os.path.join(bench.PROFILES, "pmc_wl-test.json")))
+    assert rec["calibration"]["fetch_factor"] == pytest.approx(2.0)
+    assert rec["calibration"]["write_factor"] == pytest.approx(1.0)
+    k = rec["kernels"]["k_combine<false, 1, 2>"]
+    assert k["launches"] == 2
+    assert k["hbm_bytes_per_launch"] == int(1100.0 * 1024 * 2.0 + 500.0 * 1024 * 1.0)
+    assert "vectorized_elementwise_kernel<4>" not in json.dumps(rec["kernels"])
+    # read back through the bench's lookup: the hashes match the current sources
+    assert bench.measured_traffic("k_combine", "wl-test") == k["hbm_bytes_per_launch"]
+    assert bench.measured_traffic("k_dispatch_expand", "wl-test") == \
+        int(300.0 * 1024 * 2.0 + 100.0 * 1024 * 1.0)
+    assert bench.measured_traffic("k_plan_place", "wl-test") is None
+    # a recorded hash that no longer matches its source voids the reading
+    rec["source_hashes"][bench.PMC_COMMON[0]] = "0" * 16
+    json.dump(rec, open(os.path.join(bench.PROFILES, "pmc_wl-test.json"), "w"))
+    assert bench.measured_traffic("k_combine", "wl-test") is None
+
+
+def test_trace_summary_groups_by_kernel_and_grid(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(bench.PROFILES)
+    rows = []
+    t = 0
+    for name, grid, ns, n in [(K_COMBINE, 4096, 80000, 3), (K_COMBINE, 1024, 20000, 2),
+                              (K_EXPAND, 2048, 30000, 4), (COPY, 64, 10, 1)]:
+        for _ in range(n):
+            rows.append({"Kernel_Name": name, "Grid_Size_X": grid, "Grid_Size_Y": 1,
+                         "Grid_Size_Z": 1, "Start_Timestamp": t, "End_Timestamp": t + ns})
+            t += ns + 1000
+    _write_csv(str(tmp_path / "tr" / "run_kernel_trace.csv"),
+               ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+                "End_Timestamp"], rows)
+    log = tmp_path / "b.log"
+    log.write_text("[bench] noise\n" + json.dumps(
+        {"ms_per_step": 0.2, "call_us": {"combine": 80.0}, "roofline": {"frac": 0.7}}) + "\n")
+    bench.summarize_trace("wl-test", str(tmp_path / "tr"), "the command", str(log))
+    md = open(os.path.join(bench.PROFILES, "kernels_wl-test.md")).read().splitlines()
+    table = [ln for ln in md if ln.startswith("| k_")]
+    assert table[0].startswith("| k_combine<false, 1, 2> | 4096 | 3 | 240.0 | 80.00 |")
+    assert table[1].startswith("| k_dispatch_expand<4, 1, true> | 2048 | 4 | 120.0 | 30.00 |")
+    assert table[2].startswith("| k_combine<false, 1, 2> | 1024 | 2 | 40.0 | 20.00 |")
+    assert any("more lines, each under 0.1 %" in ln for ln in md)  # the 10 ns copy
+    assert any(ln.startswith("Bench line of the same run: step 0.2 ms") for ln in md)
+    assert "    the command" in md
