@@ -59,25 +59,34 @@ class Inputs:
         self.plan = moon.moon_plan_create(ctx)
 
 
-def algorithmic_bytes(moon, ctx, plan):
-    """Bytes the method must move in dispatch and combine for this plan."""
-    c = ctx.cfg
-    R, S, K, H = c.R, c.S, c.K, c.H
-    pt = {k: v.cpu().numpy() for k, v in moon.plan_tensors(plan).items()}
+def bytes_from_counts(R, S, K, H, n_grp, n_dup, n_pad):
+    """Bytes the method must move in dispatch and combine, from a plan's
+    duplicate groups, duplicate rows and padding rows (all ranks)."""
     n_route = R * S * K
-    n_grp = int(pt["dup_counts"][:, 0].sum())
-    n_dup = int(pt["dup_counts"][:, 1].sum())
-    z = pt["zero_fill_ranges"]
-    n_pad = int((z[..., 1] - z[..., 0]).sum())
     row = 2 * H
     d_min = (row * R * S + row * n_route + row * n_pad + 4 * n_route * 3 + 4 * n_pad
              + 12 * n_grp + 4 * n_dup)
     dispatch = d_min + row * n_dup  # the epilogue re-reads each duplicate's primary
     combine = row * n_route + row * R * S + 4 * n_route * 2 + 4 * n_route  # + weight gather
     return dict(dispatch=dispatch, dispatch_minimal=d_min, combine=combine, n_route=n_route,
-                n_dup=n_dup, n_grp=n_grp, n_pad=n_pad,
-                slots_used=int(pt["remote_stats"][:, 0].sum()),
-                routes_in_slots=int(pt["remote_stats"][:, 1].sum()))
+                n_dup=n_dup, n_grp=n_grp, n_pad=n_pad)
+
+
+def plan_counts(dup_counts, zero_fill_ranges):
+    """(duplicate groups, duplicate rows, padding rows) of a plan."""
+    return (int(dup_counts[:, 0].sum()), int(dup_counts[:, 1].sum()),
+            int((zero_fill_ranges[..., 1] - zero_fill_ranges[..., 0]).sum()))
+
+
+def algorithmic_bytes(moon, ctx, plan):
+    """Bytes the method must move in dispatch and combine for this plan."""
+    c = ctx.cfg
+    pt = {k: v.cpu().numpy() for k, v in moon.plan_tensors(plan).items()}
+    nb = bytes_from_counts(c.R, c.S, c.K, c.H, *plan_counts(pt["dup_counts"],
+                                                             pt["zero_fill_ranges"]))
+    nb.update(slots_used=int(pt["remote_stats"][:, 0].sum()),
+              routes_in_slots=int(pt["remote_stats"][:, 1].sum()))
+    return nb
 
 
 def run_steps(moon, ctx, sets, steps, warmup, stream):
@@ -553,13 +562,8 @@ def cpu_baseline(config, seed, budget_s=12.0):
         t_comb += t3 - t2
         n += 1
         if n == 1:
-            n_route = R * S * K
-            n_grp, n_dup = int(pl.dup_counts[:, 0].sum()), int(pl.dup_counts[:, 1].sum())
-            n_pad = int((pl.zero_fill_ranges[..., 1] - pl.zero_fill_ranges[..., 0]).sum())
-            row = 2 * H
-            bytes_dc = (row * R * S + row * n_route + row * n_pad + 4 * n_route * 3 + 4 * n_pad
-                        + 12 * n_grp + 4 * n_dup + row * n_dup) + \
-                       (row * n_route + row * R * S + 4 * n_route * 3)
+            nb = bytes_from_counts(R, S, K, H, *plan_counts(pl.dup_counts, pl.zero_fill_ranges))
+            bytes_dc = nb["dispatch"] + nb["combine"]
         if time.perf_counter() - t_start >= budget_s:
             break
     total = t_plan + t_disp + t_comb

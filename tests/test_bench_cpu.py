@@ -8,6 +8,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import bench
@@ -123,3 +124,29 @@ def test_trace_summary_groups_by_kernel_and_grid(tmp_path, monkeypatch):
     assert any("more lines, each under 0.1 %" in ln for ln in md)  # the 10 ns copy
     assert any(ln.startswith("Bench line of the same run: step 0.2 ms") for ln in md)
     assert "    the command" in md
+
+
+def test_algorithmic_bytes_by_hand():
+    """R=2, S=3, K=2, H=8 (a row is 16 bytes), 1 duplicate group with 1
+    duplicate row, 5 padding rows: every term counted out by hand."""
+    nb = bench.bytes_from_counts(2, 3, 2, 8, n_grp=1, n_dup=1, n_pad=5)
+    routes, row, tokens = 12, 16, 6
+    d_min = (tokens * row        # each token row read once
+             + routes * row      # every route's row written
+             + 5 * row           # padding rows zeroed
+             + routes * 12       # dst read, weight read, weight written
+             + 5 * 4             # padding weights zeroed
+             + 1 * 12 + 1 * 4)   # the duplicate record and its row offset
+    assert nb["dispatch_minimal"] == d_min
+    assert nb["dispatch"] == d_min + 1 * row  # the epilogue reads the primary again
+    assert nb["combine"] == routes * row + tokens * row + routes * 12
+    assert bench.plan_counts(np.array([[1, 1], [0, 0]]),
+                             np.array([[[3, 5], [7, 7]], [[0, 3], [9, 9]]])) == (1, 1, 5)
+
+
+def test_cpu_baseline_record():
+    """The oracle timed on the host: one pass of the full workload is enough
+    to fill the record the bench line carries."""
+    rec = bench.cpu_baseline(2, 2000, budget_s=0.0)
+    assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "GB/s"
+    assert rec["value"] > 0 and " x 1: plan " in rec["sample"]
