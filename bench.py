@@ -577,7 +577,7 @@ def cpu_baseline(config, seed, budget_s=12.0):
     avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": round(bytes_dc * n / total / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "host_cpu": model, "host_cores_available": avail,
-            "sample": f"full workload (config {config}, seed {seed}) x {n}: plan "
+            "sample": f"full workload {c['name']} (seed {seed}) x {n}: plan "
                       f"{t_plan / n * 1e3:.1f} ms, dispatch {t_disp / n * 1e3:.1f} ms, combine "
                       f"{t_comb / n * 1e3:.1f} ms per step on 1 host core; "
                       f"{R * S * n / total:.0f} tokens/s"}

@@ -97,7 +97,7 @@ def workload_inputs(config, level=0):
 def test_workload_full_parity(env, config, level):
     moon, dev = env
     wl, hidden, y = workload_inputs(config, level)
-    say(f"[workload] config {config} level {level} maxvio={wl['maxvio']:.3f}")
+    say(f"[workload] {wl['name']} level {level} maxvio={wl['maxvio']:.3f}")
     run_full(moon, dev, wl["topk"], wl["w"], hidden, y, wl["R"], wl["E"], wl["K"], wl["S"],
              wl["H"], wl["B"], wl["P"], label=wl["name"])
 
