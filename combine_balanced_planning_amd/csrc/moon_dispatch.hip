@@ -15,7 +15,8 @@
 //                       primaries the epilogue re-reads, when all such rows
 //                       fit in a budget of the last-level cache); slice 0 also
 //                       scatters the K route weights.  Further items zero the
-//                       padding rows of every (rank, group), two rows each.
+//                       padding rows of a rank's home-expert and slot groups
+//                       (the only ones that can hold rows), two rows each.
 //   k_dispatch_expand   persistent grid; a work item is one wave on a 4 KB
 //                       slice of one duplicate group's primary row (plain
 //                       loads where the scatter kept the primaries in the
@@ -53,7 +54,10 @@ __global__ void __launch_bounds__(kThreads)
   const int nsl = (V + kWave * kSliceVec - 1) / (kWave * kSliceVec);
   const int64_t tok_items = (int64_t)d.R * d.S * nsl;
   const int zpg = (d.P - 1 + kZeroRows - 1) / kZeroRows;  // zero items per group
-  const int64_t items = tok_items + (int64_t)d.R * d.EB * zpg;
+  // Only a rank's own E/R home experts and its B slots can hold rows: the
+  // groups of experts homed elsewhere are always empty and get no items.
+  const int gpr = d.Eg + d.B;  // groups per rank that can hold rows
+  const int64_t items = tok_items + (int64_t)d.R * gpr * zpg;
   const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t it = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; it < items;
        it += stride) {
@@ -111,8 +115,10 @@ __global__ void __launch_bounds__(kThreads)
       if (status != 0) return;
       // Zero-fill: rows [a + kZeroRows*blk, ..) of one (rank, group) padding range.
       const int64_t z = it - tok_items;
-      const int grp = (int)(z / zpg), blk = (int)(z - (int64_t)grp * zpg);
-      const int u = grp / d.EB;
+      const int lg = (int)(z / zpg), blk = (int)(z - (int64_t)lg * zpg);
+      const int u = lg / gpr, lj = lg - u * gpr;
+      const int g = lj < d.Eg ? u * d.Eg + lj : d.E + (lj - d.Eg);
+      const int grp = u * d.EB + g;
       const int a = pa.zfr[grp * 2 + 0] + blk * kZeroRows, b = pa.zfr[grp * 2 + 1];
       const int rows = min(kZeroRows, b - a);
       if (rows <= 0) continue;
@@ -200,7 +206,7 @@ hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* 
   const int V = d.H / 8;
   const int nsl = (V + kWave * kSliceVec - 1) / (kWave * kSliceVec);
   const int zpg = (d.P - 1 + kZeroRows - 1) / kZeroRows;
-  const int64_t items = (int64_t)d.R * d.S * nsl + (int64_t)d.R * d.EB * zpg;
+  const int64_t items = (int64_t)d.R * d.S * nsl + (int64_t)d.R * (d.Eg + d.B) * zpg;
   const int64_t want = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   const int blocks = (int)(want < kScatterBlocks ? (want > 0 ? want : 1) : kScatterBlocks);
   // The epilogue re-reads one primary row per duplicate group (about 1.3
