@@ -144,6 +144,7 @@ EDGE = [
     ("b-small-ok", 4, 16, 2, 64, 16, 1, 4, "uniform"),
     ("large-e", 8, 512, 8, 128, 16, 0, 8, "skewed"),
     ("max-tiles-e512", 32, 512, 8, 1024, 16, 0, 4, "skewed"),  # 256 planner tiles
+    ("max-width", 2, 8, 3, 12, 65536, 0, 4, "repeats"),  # the widest rows accepted
 ]
 
 
