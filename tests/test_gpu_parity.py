@@ -145,6 +145,8 @@ EDGE = [
     ("large-e", 8, 512, 8, 128, 16, 0, 8, "skewed"),
     ("max-tiles-e512", 32, 512, 8, 1024, 16, 0, 4, "skewed"),  # 256 planner tiles
     ("max-width", 2, 8, 3, 12, 65536, 0, 4, "repeats"),  # the widest rows accepted
+    # 18 chunks per planner wave: more than a wave stages in LDS at once
+    ("long-waves", 2, 16, 64, 35000, 8, 0, 4, "repeats"),
 ]
 
 
