@@ -382,6 +382,30 @@ def test_histogram_check_every_expert(env, R, E, K, S):
         moon.moon_ctx_destroy(ctx)
 
 
+def test_call_tag_wraps(env):
+    """Tiles exchange duplicate counts in words tagged with the low 16 bits of
+    a per-context call counter; planning past the point where the tag wraps
+    still gives the oracle's plan, call after call."""
+    moon, dev = env
+    R, E, K, S, H, B, P = 2, 8, 2, 300, 8, 0, 4  # two tiles per rank
+    rng = np.random.default_rng(4242)
+    topks = [_edge_topk(rng, R, S, K, E, m) for m in ("uniform", "repeats")]
+    refs = [oracle.plan(t, E, E // R, P) for t in topks]
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    plan = moon.moon_plan_create(ctx)
+    try:
+        ts = [pt.to_dev(t, dev) for t in topks]
+        say("[case] call tag wrap: 65540 planning calls")
+        for i in range(65540):
+            moon.moon_plan(ctx, ts[i % 2], None, plan)
+            if i >= 65530 or i < 2:
+                assert moon.moon_plan_status(plan) == moon.MOON_OK, i
+                pt.compare_plan(pt.gpu_plan_arrays(plan), refs[i % 2])
+    finally:
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
+
+
 def test_plan_mismatch_is_rejected(env):
     moon, dev = env
     c1 = moon.moon_ctx_create(2, 8, 2, 8, 16, 4, 2)
