@@ -51,6 +51,10 @@ SMALL = [
     ("r8-skewed", 8, 64, 6, 256, 8, 16, 1.5, [(64, 32)]),
     ("r16-hot", 16, 64, 8, 128, 4, 8, 3.0, [(8, 8), (4, 4), (2048,)]),
     ("b-small", 4, 16, 2, 64, 2, 4, 1.0, [(16,)]),
+    # more than 64 slots: the copy lists the used slots first (1, 2 and 32 rounds)
+    ("slots-256", 8, 256, 8, 256, 32, 16, 2.0, [(8, 8), (100,)]),
+    ("slots-512", 16, 512, 8, 128, 32, 8, 2.5, [(16,), (8, 4)]),
+    ("slots-8192", 32, 512, 4, 64, 256, 4, 3.0, [(8,)]),
 ]
 
 
