@@ -470,11 +470,18 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk,
   }
   // Per-wave expert counts of the tile (recounted from the routes).
   wave_lds_fence();
-  for (int cc = 0; cc < nchunks; ++cc) {
-    const int tok = ws0 + cc * ctok;
-    const int nl = min(ctok, ws1 - tok) * K;
-    if (lane < nl) {
-      const int e = staged ? st[cc * kWave + lane] : topk[(rowbase + tok) * K + lane];
+  // (separate loops for LDS and global reads: a read through a pointer to
+  // either becomes a flat load, which waits for every outstanding access)
+  if (staged) {
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int e = st[cc * kWave + lane];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&run[e], 1);
+    }
+  } else {
+    for (int cc = 0; cc < nchunks; ++cc) {
+      const int tok = ws0 + cc * ctok;
+      const int nl = min(ctok, ws1 - tok) * K;
+      const int e = lane < nl ? topk[(rowbase + tok) * K + lane] : -1;
       if ((unsigned)e < (unsigned)E) atomicAdd(&run[e], 1);
     }
   }
@@ -681,7 +688,11 @@ __device__ void place_tile(const Dims& d, const int32_t* __restrict__ topk,
     const int nl = min(ctok, ws1 - tok) * K;
     const bool act = lane < nl;
     int v = 0;
-    if (act) v = staged ? st[c * kWave + lane] : pa.dst[(rowbase + tok) * K + lane];
+    if (staged) {  // (two reads, not one through a selected pointer: see above)
+      if (act) v = st[c * kWave + lane];
+    } else {
+      if (act) v = pa.dst[(rowbase + tok) * K + lane];
+    }
     const int G = dst_row(v);
     const int u = act ? G / NvS : -1;
     const int uk = act ? u : 0;
