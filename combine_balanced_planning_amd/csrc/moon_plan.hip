@@ -211,7 +211,8 @@ __device__ __forceinline__ void load_count_batch(const Dims& d, const Scratch& s
     c[j][1] = v.y;
     c[j][2] = v.z;
     c[j][3] = v.w;
-    given[j] = (e < d.E && ((chk >> (e / kPlanWaves)) & 1u) && lane < d.R) ? tpe[lane * d.E + e] : 0;
+    const bool want = e < d.E && ((chk >> (e / kPlanWaves)) & 1u) && lane < d.R;
+    given[j] = want ? tpe[lane * d.E + e] : 0;
   }
 }
 

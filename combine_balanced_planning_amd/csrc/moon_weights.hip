@@ -41,7 +41,8 @@ constexpr int kIndexThreads = 1024;
 // Chosen by a sweep on MI355X.  The copy loads expert rows through the
 // caches: slots on several ranks often hold the same expert, and later
 // copies of it then hit in the cache (non-temporal loads were 1.5x slower).
-static_assert(kMaxSlotsTotal <= 65536 && kMaxE <= 32768, "a used slot and its expert pack into one int");
+static_assert(kMaxSlotsTotal <= 65536 && kMaxE <= 32768,
+              "a used slot and its expert pack into one int");
 constexpr int kCopyVec = 8;          // 16-byte vectors per lane per copy chunk (8 KB per wave)
 constexpr int kCopyBlocks = 8192;
 constexpr bool kCopyNtLoad = false;
