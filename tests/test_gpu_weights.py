@@ -55,6 +55,9 @@ SMALL = [
     ("slots-256", 8, 256, 8, 256, 32, 16, 2.0, [(8, 8), (100,)]),
     ("slots-512", 16, 512, 8, 128, 32, 8, 2.5, [(16,), (8, 4)]),
     ("slots-8192", 32, 512, 4, 64, 256, 4, 3.0, [(8,)]),
+    # the most tensors one call takes (gate, up, down and five more)
+    ("eight-tensors", 4, 16, 4, 96, 4, 4, 2.0,
+     [(8, 4), (16,), (4, 4), (24,), (8,), (4, 4), (32,), (12,)]),
 ]
 
 
