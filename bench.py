@@ -5,7 +5,8 @@ plan (histogram, balance, layout, placement, duplicate records) -> dispatch
 (scatter + zero-fill + dedup epilogue) -> combine (weighted K-sum + weight
 gather) -> prefetch index.  Inputs are resident in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3] [--step-only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload r8-e64-k6|dsv3|r16-e384-k8]
+                    [--step-only]
 
 Prints one JSON line.  `value` is the dispatch+combine algorithmic HBM bytes
 of a step divided by the measured time of the whole step (plan included), in
@@ -45,7 +46,7 @@ class Inputs:
 
         import synth
         import synth.gpu as sg
-        c = synth.CONFIGS[config]
+        c = synth.WORKLOADS[synth.workload_id(config)]
         R, E, K, S, H = c["R"], c["E"], c["K"], c["S"], c["H"]
         topk, w = synth.routing(config, seed, alpha)
         self.maxvio = synth.maxvio(topk, E)
@@ -228,14 +229,15 @@ def measure_ablations(moon, ctx, s, nb, stream, iters):
     }
 
 
-# maxvio sweeps: workload -> (configuration of the skewed levels, levels);
-# r8-e64-k6 sweeps the skewed configuration of its shapes, the large
-# R=16 configuration its own levels 1.. (level 0 is the timed base run).
-SWEEPS = {2: (4, [0, 1, 2, 3]), 5: (5, [1, 2, 3, 4])}
+# maxvio sweeps: workload -> (workload of the skewed levels, levels);
+# r8-e64-k6 sweeps the skewed workload of its shapes, the large R=16
+# workload its own levels 1.. (level 0 is the timed base run).
+SWEEPS = {"r8-e64-k6": ("r8-e64-k6-skewed", [0, 1, 2, 3]),
+          "r16-e384-k8": ("r16-e384-k8", [1, 2, 3, 4])}
 
 # Expert FFN intermediate width H' per workload: DeepSeek-V3's expert width for
 # the DSv3-shaped workload; H/2 (a reading: the pages give none) for r8-e64-k6.
-FFN_WIDTH = {2: 1024, 3: 2048}
+FFN_WIDTH = {"r8-e64-k6": 1024, "dsv3": 2048}
 
 
 def measure_weights(moon, ctx, s, stream, iters, hp):
@@ -539,7 +541,7 @@ def cpu_baseline(config, seed, budget_s=12.0):
     full workload, repeated until about `budget_s` seconds have passed."""
     import oracle
     import synth
-    c = synth.CONFIGS[config]
+    c = synth.WORKLOADS[synth.workload_id(config)]
     R, E, K, S, H, B, P = (c[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
     topk, w = synth.routing(config, seed)
     hidden = synth.hidden_bf16(seed, R, S, H)
@@ -588,7 +590,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--workload", default="r8-e64-k6", choices=["r8-e64-k6", "dsv3", "r16-e384-k8"])
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
@@ -609,7 +611,7 @@ def main():
     args = ap.parse_args()
     if args.summarize_pmc or args.summarize_trace:
         import synth
-        name = synth.CONFIGS[args.workload]["name"]
+        name = synth.WORKLOADS[synth.workload_id(args.workload)]["name"]
         if args.summarize_pmc:
             summarize_pmc(name, args.summarize_pmc, args.commands)
         else:
@@ -640,7 +642,7 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     config = args.workload
-    c = synth.CONFIGS[config]
+    c = synth.WORKLOADS[synth.workload_id(config)]
     R, E, K, S, H, B, P = (c[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
     log(f"[bench] workload {c['name']}: building inputs")
     ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
@@ -693,7 +695,7 @@ def main():
             log("[bench] weight prefetch and gradient reduction")
             weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
                                       FFN_WIDTH[config])
-        if config == 2:
+        if config == "r8-e64-k6":
             log("[bench] padded serving workload")
             serving = measure_serving(moon, dev, stream, max(10, args.steps // 5), 3)
 
@@ -705,7 +707,7 @@ def main():
                       "GBps": round(value, 1), "tokens_per_s": round(R * S / (ms_step * 1e-3))})
         sc, levels = SWEEPS[config]
         for level in levels:
-            target = synth.LEVELS[sc][level]
+            target = synth.LEVELS[synth.workload_id(sc)][level]
             log(f"[bench] maxvio level {target}")
             s4 = [Inputs(moon, ctx, sc, synth.seed_of(sc, level), synth.alpha_for(sc, level), dev),
                   Inputs(moon, ctx, sc, synth.seed_of(sc, level) + 500,

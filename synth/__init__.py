@@ -152,9 +152,10 @@ def normal_f64(key_a, key_b, count):
 
 
 # ---------------------------------------------------------------------------
-# Workloads.  Shapes of the five configurations; `dedup_stress` makes every
-# odd token choose all K experts among one uniformly drawn home rank.
-CONFIGS = {
+# Workloads, by a stable integer id (it enters the seeds: seed = 1000 * id +
+# level) and by name; `dedup_stress` makes every odd token choose all K
+# experts among one uniformly drawn home rank.
+WORKLOADS = {
     1: dict(name="tiny", R=2, E=8, K=2, S=64, H=128, P=8, B=4, dedup_stress=False),
     2: dict(name="r8-e64-k6-s2048-h2048", R=8, E=64, K=6, S=2048, H=2048, P=16, B=8,
             dedup_stress=False),
@@ -175,16 +176,35 @@ CONFIGS = {
 SERVING = dict(name="serving-padded-r8-e256-k8-h7168", R=8, E=256, K=8, H=7168, P=128, B=32,
                max_tokens=4096, min_capacity=128, invalid_every=64, dedup_stress=False)
 SERVING_LEVELS = [dict(name="decode", lo=48, hi=200), dict(name="prefill", lo=1200, hi=3000)]
-SERVING_CONFIG = 6
+# Serving seeds are 6000 + level, clear of the workloads' 1000 * id + level.
+_SERVING_SEED_BASE = 6000
 
-# maxvio targets per configuration (level index -> target); None = no bias.
+# Short names accepted beside the full ones.
+_ALIASES = {"r8-e64-k6": 2, "dsv3": 3, "r8-e64-k6-skewed": 4, "r16-e384-k8": 5}
+
+
+def workload_id(key):
+    """The integer id of a workload given by id, full name or short name."""
+    if isinstance(key, (int, np.integer)):
+        if int(key) not in WORKLOADS:
+            raise KeyError(f"no workload {key}")
+        return int(key)
+    if key in _ALIASES:
+        return _ALIASES[key]
+    for i, c in WORKLOADS.items():
+        if c["name"] == key:
+            return i
+    raise KeyError(f"no workload named {key!r}")
+
+
+# maxvio targets per workload id (level index -> target); None = no bias.
 LEVELS = {1: [None], 2: [None], 3: [None], 4: [0.5, 1.0, 2.0, 4.0], 5: [None, 1.0, 2.0, 4.0, 8.0]}
 
 _ALPHA_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "alpha_table.json")
 
 
 def seed_of(config, level=0):
-    return 1000 * int(config) + int(level)
+    return 1000 * workload_id(config) + int(level)
 
 
 def maxvio(topk, E):
@@ -244,7 +264,7 @@ def route_from_logits(c, seed, logits, alpha):
 
 def routing(config, seed, alpha=0.0, cfg=None):
     """Top-K routing for one run: returns (topk [R,S,K] int32, weights [R,S,K] fp32)."""
-    c = dict(CONFIGS[config]) if cfg is None else dict(cfg)
+    c = dict(WORKLOADS[workload_id(config)]) if cfg is None else dict(cfg)
     return route_from_logits(c, seed, base_logits(c, seed), alpha)
 
 
@@ -256,20 +276,24 @@ def load_alpha_table():
 
 
 def alpha_for(config, level):
-    """Bias strength for a configuration's maxvio level (0.0 when unbiased)."""
+    """Bias strength for a workload's maxvio level (0.0 when unbiased)."""
+    config = workload_id(config)
     target = LEVELS[config][level]
     if target is None:
         return 0.0
     tab = load_alpha_table()
     key = f"{config}:{level}"
     if key not in tab:
-        raise KeyError(f"no tuned alpha for config {config} level {level}; run python -m synth.tune")
+        raise KeyError(f"no tuned alpha for {WORKLOADS[config]['name']} level {level}; "
+                       "run python -m synth.tune")
     return float(tab[key]["alpha"])
 
 
 def workload(config, level=0):
-    """Routing of one configuration and maxvio level: dict with shapes, topk, w, maxvio."""
-    c = dict(CONFIGS[config])
+    """Routing of one workload (id or name) and maxvio level: dict with shapes,
+    topk, w, maxvio."""
+    config = workload_id(config)
+    c = dict(WORKLOADS[config])
     seed = seed_of(config, level)
     alpha = alpha_for(config, level)
     topk, w = routing(config, seed, alpha)
@@ -301,7 +325,7 @@ def serving_workload(level, n_tok=None):
     `n_tok` overrides the drawn per-rank real token counts."""
     c = dict(SERVING)
     lv = SERVING_LEVELS[level]
-    seed = seed_of(SERVING_CONFIG, level)
+    seed = _SERVING_SEED_BASE + int(level)
     R, E, K = c["R"], c["E"], c["K"]
     span = np.uint64(lv["hi"] - lv["lo"] + 1)
     if n_tok is None:
@@ -321,7 +345,7 @@ def serving_workload(level, n_tok=None):
     tpe = np.stack([np.bincount(topk[r].reshape(-1), minlength=E) for r in range(R)])
     c.update(seed=seed, level=level, level_name=lv["name"], n_tok=n_tok, topk=topk, w=w,
              tokens_per_expert=tpe.astype(np.int32), maxvio=maxvio(topk, E),
-             config=SERVING_CONFIG)
+             config=SERVING["name"])
     return c
 
 

@@ -14,7 +14,7 @@ import synth
 
 
 def tune(config, level, tol=0.02):
-    c = dict(synth.CONFIGS[config])
+    c = dict(synth.WORKLOADS[config])
     target = synth.LEVELS[config][level]
     seed = synth.seed_of(config, level)
     base = synth.base_logits(c, seed)

@@ -52,7 +52,8 @@ def sample_rows(rng, ref, src, n_routes=2048, n_groups=4):
     return np.array(sorted(rows), np.int64)
 
 
-@pytest.mark.parametrize("config,level", [(3, 0), (5, 0), (5, 2), (5, 4)])
+@pytest.mark.parametrize("config,level", [("dsv3", 0), ("r16-e384-k8", 0),
+                                          ("r16-e384-k8", 2), ("r16-e384-k8", 4)])
 def test_full_size_sampled_parity(env, config, level):
     import torch
 

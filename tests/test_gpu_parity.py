@@ -93,7 +93,8 @@ def workload_inputs(config, level=0):
     return wl, hidden, y
 
 
-@pytest.mark.parametrize("config,level", [(1, 0), (2, 0), (4, 0), (4, 1), (4, 2), (4, 3)])
+@pytest.mark.parametrize("config,level", [("tiny", 0), ("r8-e64-k6", 0)] +
+                         [("r8-e64-k6-skewed", lv) for lv in range(4)])
 def test_workload_full_parity(env, config, level):
     moon, dev = env
     wl, hidden, y = workload_inputs(config, level)
@@ -171,7 +172,7 @@ def test_fused_duplicates_and_unweighted_round_trip(env):
     dispatched windows gives K * x exactly (closed form)."""
     import torch
     moon, dev = env
-    wl, hidden, _ = workload_inputs(2)
+    wl, hidden, _ = workload_inputs("r8-e64-k6")
     R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
     say(f"[case] fused + round trip {wl['name']}")
     ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
@@ -199,7 +200,7 @@ def test_clone_repeat_and_backward_reuse(env):
     tensor with an existing plan (the backward path) needs no new planning."""
     import torch
     moon, dev = env
-    wl, hidden, _ = workload_inputs(1)
+    wl, hidden, _ = workload_inputs("tiny")
     R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
     ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
     p1, p2 = moon.moon_plan_create(ctx), moon.moon_plan_create(ctx)

@@ -104,7 +104,8 @@ def run_prologue(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, weighted, i
         moon.moon_ctx_destroy(ctx)
 
 
-@pytest.mark.parametrize("config,level", [(1, 0), (2, 0), (4, 3)])
+@pytest.mark.parametrize("config,level", [("tiny", 0), ("r8-e64-k6", 0),
+                                          ("r8-e64-k6-skewed", 3)])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_prologue_workloads(env, config, level, weighted):
     moon, dev = env

@@ -191,7 +191,7 @@ def test_weights_reject_bad_shapes(env):
 HP = 2048  # expert FFN intermediate width H' of the DSv3-shaped and R=16 workloads
 
 
-@pytest.mark.parametrize("config,level", [(3, 0), (5, 4)])
+@pytest.mark.parametrize("config,level", [("dsv3", 0), ("r16-e384-k8", 4)])
 def test_weights_full_size(env, config, level):
     """One projection at the workload's real shape: [E, H, H'] bf16 weights and
     [E, H, H'] fp32 gradients with the slots the workload's plan uses."""

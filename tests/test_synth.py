@@ -43,16 +43,17 @@ def test_topk_ties_choose_lower_expert_first():
 
 
 def test_routing_recipe_tiny():
-    topk, w = synth.routing(1, synth.seed_of(1))
+    topk, w = synth.routing("tiny", synth.seed_of("tiny"))
     assert topk.shape == (2, 64, 2) and w.shape == (2, 64, 2)
     assert ((topk >= 0) & (topk < 8)).all()
     assert (topk[..., 0] != topk[..., 1]).all()
     assert np.allclose(w.sum(-1), 1.0, atol=1e-6) and (w[..., 0] >= w[..., 1]).all()
-    t2, w2 = synth.routing(1, synth.seed_of(1))
+    t2, w2 = synth.routing("tiny", synth.seed_of("tiny"))
     assert (t2 == topk).all() and (w2 == w).all()
 
 
 def test_skewed_levels_hit_their_targets():
-    for level, target in enumerate(synth.LEVELS[4]):
-        wl = synth.workload(4, level)
+    skewed = synth.workload_id("r8-e64-k6-skewed")
+    for level, target in enumerate(synth.LEVELS[skewed]):
+        wl = synth.workload("r8-e64-k6-skewed", level)
         assert abs(wl["maxvio"] - target) <= 0.02 * target, (level, wl["maxvio"])
