@@ -32,5 +32,27 @@ def build(verbose=False):
     return SO
 
 
+# A C11 program that uses libmoon.so through include/moon.h only (hipMalloc'd
+# pointers, no Python); the GPU tests run it.  Host code, built with gcc.
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi_example.c")
+C_EXAMPLE_BIN = os.path.join(ROOT, "tests", "c_abi_example.bin")
+
+
+def build_c_example(verbose=False):
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_EXAMPLE_SRC, "-o", C_EXAMPLE_BIN + ".tmp", "-L", HERE, "-lmoon",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../combine_balanced_planning_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(C_EXAMPLE_BIN + ".tmp", C_EXAMPLE_BIN)
+    return C_EXAMPLE_BIN
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_c_example(verbose=True)
