@@ -83,9 +83,11 @@ _lib.moon_prefetch_weight.argtypes = [_vp, _vp, _P(moon_weight_tensor), _i32, _v
 _lib.moon_reduce_grad.argtypes = [_vp, _vp, _P(moon_grad_tensor), _i32, _vp]
 _lib.moon_status_str.argtypes = [_i32]
 _lib.moon_status_str.restype = ctypes.c_char_p
+_lib.moon_debug_tile_counts.argtypes = [_vp, _vp, _P(_i32), _P(_i32), _vp]
 for _f in ("moon_ctx_create", "moon_ctx_layout", "moon_plan_create", "moon_plan_clone",
            "moon_plan_view", "moon_plan_status", "moon_plan", "moon_dispatch", "moon_combine",
-           "moon_prefetch_index", "moon_prefetch_weight", "moon_reduce_grad"):
+           "moon_prefetch_index", "moon_prefetch_weight", "moon_reduce_grad",
+           "moon_debug_tile_counts"):
     getattr(_lib, _f).restype = _i32
 
 
@@ -228,6 +230,21 @@ def moon_prefetch_index(ctx, plan, out, stream=None):
     _check(_lib.moon_prefetch_index(ctx.ptr, plan.ptr,
                                     _ptr(out, torch.int32, c.R * ctx.B * 2, "out"),
                                     _stream(stream)), "moon_prefetch_index")
+
+
+def moon_debug_tile_counts(ctx, out=None, stream=None):
+    """Test hook: the planner's per-tile histogram of the latest moon_plan call
+    (see include/moon.h).  Returns (tile_tokens, tiles_per_rank); when `out`
+    (int32 [E+1, R*tiles_per_rank] on the GPU) is given, fills it."""
+    c = ctx.cfg
+    tt, tpr = _i32(0), _i32(0)
+    _check(_lib.moon_debug_tile_counts(ctx.ptr, None, ctypes.byref(tt), ctypes.byref(tpr), None),
+           "moon_debug_tile_counts")
+    if out is not None:
+        n = (c.E + 1) * c.R * tpr.value
+        _check(_lib.moon_debug_tile_counts(ctx.ptr, _ptr(out, torch.int32, n, "out"), None, None,
+                                           _stream(stream)), "moon_debug_tile_counts")
+    return tt.value, tpr.value
 
 
 def _expert_pair(ctx, rows, slots, name, dtype=None):

@@ -342,6 +342,22 @@ moon_status moon_plan_status(const moon_comm_plan* plan, hipStream_t stream) {
   return bits == 0 ? MOON_OK : MOON_ERR_INTERNAL;
 }
 
+moon_status moon_debug_tile_counts(const moon_ctx* ctx, int32_t* counts_dev, int32_t* tile_tokens,
+                                   int32_t* tiles_per_rank, hipStream_t stream) {
+  if (!ctx_ok(ctx) || !aligned(counts_dev, 4)) return MOON_ERR_INVALID_ARG;
+  const Dims& d = ctx->d;
+  if (tile_tokens != nullptr) *tile_tokens = d.tile_tok;
+  if (tiles_per_rank != nullptr) *tiles_per_rank = d.tiles_per_rank;
+  if (counts_dev == nullptr) return MOON_OK;
+  DeviceGuard g(ctx->device);
+  // the count matrix rows are ntiles_pad wide; the copy drops the padding
+  const size_t w = (size_t)d.ntiles * sizeof(int32_t);
+  if (hipMemcpy2DAsync(counts_dev, w, ctx->sc.tile_cnt, (size_t)d.ntiles_pad * sizeof(int32_t), w,
+                       (size_t)d.E + 1, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
 moon_status moon_plan(moon_ctx* ctx, const int32_t* topk_rsk, const int32_t* tokens_per_expert_re,
                       moon_comm_plan* plan, hipStream_t stream) {
   if (!ctx_ok(ctx) || !plan_ok(plan) || topk_rsk == nullptr) return MOON_ERR_INVALID_ARG;

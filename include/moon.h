@@ -237,6 +237,20 @@ moon_status moon_reduce_grad(moon_ctx* ctx, const moon_comm_plan* plan,
 
 const char* moon_status_str(moon_status s);
 
+/* Test hook, not part of the pages' interface: the planner's intermediate
+ * per-tile histogram from the latest moon_plan call of this context.  The
+ * planner cuts each rank's S tokens into *tiles_per_rank consecutive tiles of
+ * *tile_tokens tokens (the last one may be shorter); tile t = r*tiles_per_rank
+ * + i covers tokens [i*tile_tokens, min(S, (i+1)*tile_tokens)) of rank r.
+ * counts_dev (optional, caller-owned device memory) is [E+1, R*tiles_per_rank]
+ * int32: row e < E receives the routes to expert e in each tile, row E a 1 for
+ * each tile that holds an id outside [0, E) and 0 otherwise.  A
+ * device-to-device copy on `stream`, ordered after the moon_plan call when
+ * both are on the same stream.  tile_tokens and tiles_per_rank are host
+ * pointers and may be NULL. */
+moon_status moon_debug_tile_counts(const moon_ctx* ctx, int32_t* counts_dev, int32_t* tile_tokens,
+                                   int32_t* tiles_per_rank, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
