@@ -67,7 +67,7 @@ def combine_bound(acc, absum, K):
 def check_combine(out_bits, ref_out_bits, ref_acc, absum, K):
     """Combine against the oracle: bit for bit with its fp32 result (the pages
     accumulate combine in fp32: ascending k, separate multiply and add, one
-    rounding to bf16), within the benchmark spec's tolerance |d| <= 1e-2 max|ref| +
+    rounding to bf16), within the combine tolerance |d| <= 1e-2 max|ref| +
     1e-3, and within the derived bound of the exact (float64) sum."""
     o = bits_to_f32(out_bits).astype(np.float64)
     e = bits_to_f32(ref_out_bits).astype(np.float64)

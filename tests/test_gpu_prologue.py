@@ -2,7 +2,7 @@
 
 The folded primary rows the prologue stores in the context window must equal
 the oracle's bit for bit (the fold is an fp32 sum in a fixed order, rounded
-once); the combine output must stay within the benchmark spec's tolerance of the
+once); the combine output must stay within |d| <= 1e-2 max|ref| + 1e-3 of the
 oracle's and within the derived fp32 bound; the gathered weights are
 bit-exact.  Checked with y in a caller buffer (the window keeps its
 dispatched rows except at folded primaries) and with y being the window
