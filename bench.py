@@ -67,7 +67,9 @@ def bytes_from_counts(R, S, K, H, n_grp, n_dup, n_pad):
     row = 2 * H
     d_min = (row * R * S + row * n_route + row * n_pad + 4 * n_route * 3 + 4 * n_pad
              + 12 * n_grp + 4 * n_dup)
-    dispatch = d_min + row * n_dup  # the epilogue re-reads each duplicate's primary
+    # the epilogue reads each duplicate group's primary row once and writes
+    # it to the group's duplicate rows (their writes are counted above)
+    dispatch = d_min + row * n_grp
     combine = row * n_route + row * R * S + 4 * n_route * 2 + 4 * n_route  # + weight gather
     return dict(dispatch=dispatch, dispatch_minimal=d_min, combine=combine, n_route=n_route,
                 n_dup=n_dup, n_grp=n_grp, n_pad=n_pad)

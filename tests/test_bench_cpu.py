@@ -127,18 +127,18 @@ def test_trace_summary_groups_by_kernel_and_grid(tmp_path, monkeypatch):
 
 
 def test_algorithmic_bytes_by_hand():
-    """R=2, S=3, K=2, H=8 (a row is 16 bytes), 1 duplicate group with 1
-    duplicate row, 5 padding rows: every term counted out by hand."""
-    nb = bench.bytes_from_counts(2, 3, 2, 8, n_grp=1, n_dup=1, n_pad=5)
-    routes, row, tokens = 12, 16, 6
+    """R=2, S=3, K=3, H=8 (a row is 16 bytes), 1 duplicate group with 2
+    duplicate rows, 5 padding rows: every term counted out by hand."""
+    nb = bench.bytes_from_counts(2, 3, 3, 8, n_grp=1, n_dup=2, n_pad=5)
+    routes, row, tokens = 18, 16, 6
     d_min = (tokens * row        # each token row read once
              + routes * row      # every route's row written
              + 5 * row           # padding rows zeroed
              + routes * 12       # dst read, weight read, weight written
              + 5 * 4             # padding weights zeroed
-             + 1 * 12 + 1 * 4)   # the duplicate record and its row offset
+             + 1 * 12 + 2 * 4)   # the duplicate record and its two row offsets
     assert nb["dispatch_minimal"] == d_min
-    assert nb["dispatch"] == d_min + 1 * row  # the epilogue reads the primary again
+    assert nb["dispatch"] == d_min + 1 * row  # the epilogue reads the group's primary once
     assert nb["combine"] == routes * row + tokens * row + routes * 12
     assert bench.plan_counts(np.array([[1, 1], [0, 0]]),
                              np.array([[[3, 5], [7, 7]], [[0, 3], [9, 9]]])) == (1, 1, 5)
