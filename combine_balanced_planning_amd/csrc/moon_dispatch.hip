@@ -8,11 +8,12 @@
 // The rank windows are one HBM array, so the remote store of the pages is a
 // scatter of 16-byte vectors.  Bound: HBM bandwidth.
 //
-//   k_dispatch_scatter  persistent grid; a work item is one wave on a 2 KB
-//                       slice (128 vectors) of one token's row, read once
-//                       with plain loads and stored with non-temporal stores
-//                       to each primary row of the token (cached stores for
-//                       primaries the epilogue re-reads, when all such rows
+//   k_dispatch_scatter  persistent grid; a work item is one wave on a 7 KB
+//                       slice (448 vectors; a row of up to 7 KB is one item)
+//                       of one token's row, read once with plain loads and
+//                       stored with non-temporal stores to each primary row
+//                       of the token (cached stores for primaries the
+//                       epilogue re-reads, when all such rows
 //                       fit in a budget of the last-level cache); slice 0 also
 //                       scatters the K route weights.  Further items zero the
 //                       padding rows of a rank's home-expert and slot groups
@@ -32,7 +33,12 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
-constexpr int kSliceVec = 2;       // 16-byte vectors per lane in a scatter slice
+// 16-byte vectors per lane in a scatter slice.  Measured (dispatch µs,
+// widths 2 / 4 / 7 / 8 / 14): r8-e64-k6 94.8 / 87.1 / 86.0 / 85.9 / 86.3,
+// where 7 makes a 4 KB row one item; DSv3 shape 1044 / 1056 / 1048 / 1051 /
+// 1069; R=16 shape 3880 / 4306 / 3875 / 3886 / 3874, where 4 leaves the
+// last of four slices of a 14 KB row half empty.
+constexpr int kSliceVec = 7;
 // Padding rows per zero-fill item (a sweep of 1, 2, 4, 8, 16: 2 is 5 % faster
 // than 8 at serving decode, where padding dominates, and equal elsewhere).
 constexpr int kZeroRows = 2;
@@ -74,10 +80,11 @@ __global__ void __launch_bounds__(kThreads)
       const int c0 = sl * kWave * kSliceVec;
       const u32x4* src = hidden + t * V;
       u32x4 buf[kSliceVec];
+      // (non-temporal loads: 1 % slower at the DSv3 and R=16 shapes)
 #pragma unroll
       for (int c = 0; c < kSliceVec; ++c) {
         const int j = c0 + c * kWave + lane;
-        if (j < V) buf[c] = src[j];  // (non-temporal loads: 1 % slower at DSv3 and R=16)
+        if (j < V) buf[c] = src[j];
       }
       if (status != 0) return;
       if (wlane) wwin[dst_global_row(dl)] = wk;
