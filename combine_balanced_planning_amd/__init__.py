@@ -33,8 +33,9 @@ MOON_ERR_NOT_PLANNED = -10
 MOON_ERR_INTERNAL = -11
 
 MOON_COMBINE_WEIGHTED = 0x1
-MOON_DISPATCH_FUSED_DUPS = 0x2
+MOON_DISPATCH_FUSED_DUPS = 0x2  # the default dispatch, named explicitly
 MOON_COMBINE_DUP_PROLOGUE = 0x4
+MOON_DISPATCH_DEDUP_EPILOGUE = 0x8
 
 _i32, _u32, _vp = ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p
 
@@ -53,7 +54,8 @@ class moon_plan_arrays(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("dst", "experts_to_copy", "zero_fill_ranges", "remote_stats",
                                    "dup_groups", "dup_loffs", "dup_counts", "cu_seqlens",
                                    "status")] + \
-               [(n, _i32) for n in ("N", "R", "E", "B", "NvS", "K")]
+               [(n, _i32) for n in ("N", "R", "E", "B", "NvS", "K")] + \
+               [("prefetch_index", _vp)]
 
 
 class moon_weight_tensor(ctypes.Structure):
@@ -316,7 +318,8 @@ def plan_tensors(plan):
     dev = torch.device("cuda", plan.ctx.device)
     shapes = {"dst": (R, v.N), "experts_to_copy": (R, v.B), "zero_fill_ranges": (R, EB, 2),
               "remote_stats": (R, 2), "dup_groups": (R, NvS, 3), "dup_loffs": (R, NvS),
-              "dup_counts": (R, 2), "cu_seqlens": (R, EB), "status": (1,)}
+              "dup_counts": (R, 2), "cu_seqlens": (R, EB), "status": (1,),
+              "prefetch_index": (R, v.B, 2)}
     return {k: device_view(getattr(v, k), s, torch.int32, dev) for k, s in shapes.items()}
 
 

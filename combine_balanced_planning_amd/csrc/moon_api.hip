@@ -126,7 +126,7 @@ size_t carve(size_t& off, size_t bytes) {
 
 // Offsets of the plan arrays inside one allocation.
 struct PlanOffsets {
-  size_t dst, etc, zfr, rstats, dup_groups, dup_loffs, dup_counts, cu, status, total;
+  size_t dst, etc, zfr, rstats, dup_groups, dup_loffs, dup_counts, cu, status, pidx, total;
 };
 
 PlanOffsets plan_offsets(const Dims& d) {
@@ -142,6 +142,7 @@ PlanOffsets plan_offsets(const Dims& d) {
   o.dup_counts = carve(off, (size_t)d.R * 2 * i4);
   o.cu = carve(off, (size_t)d.R * d.EB * i4);
   o.status = carve(off, i4);
+  o.pidx = carve(off, (size_t)d.R * d.B * 2 * i4);
   o.total = (off + 255) & ~(size_t)255;
   return o;
 }
@@ -158,6 +159,7 @@ moon::PlanArrays plan_arrays(void* mem, const PlanOffsets& o) {
   a.dup_counts = reinterpret_cast<int32_t*>(b + o.dup_counts);
   a.cu = reinterpret_cast<int32_t*>(b + o.cu);
   a.status = reinterpret_cast<int32_t*>(b + o.status);
+  a.pidx = reinterpret_cast<int32_t*>(b + o.pidx);
   return a;
 }
 
@@ -318,6 +320,7 @@ moon_status moon_plan_view(const moon_comm_plan* plan, moon_plan_arrays* out) {
   out->dup_counts = plan->a.dup_counts;
   out->cu_seqlens = plan->a.cu;
   out->status = plan->a.status;
+  out->prefetch_index = plan->a.pidx;
   out->N = d.S * d.K;
   out->R = d.R;
   out->E = d.E;
@@ -375,7 +378,9 @@ moon_status moon_dispatch(moon_ctx* ctx, const moon_comm_plan* plan, const void*
                           uint32_t flags, hipStream_t stream) {
   if (!ctx_ok(ctx) || !plan_ok(plan) || hidden_rsh == nullptr) return MOON_ERR_INVALID_ARG;
   if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
-  if ((flags & ~MOON_DISPATCH_FUSED_DUPS) != 0) return MOON_ERR_INVALID_ARG;
+  if ((flags & ~(MOON_DISPATCH_FUSED_DUPS | MOON_DISPATCH_DEDUP_EPILOGUE)) != 0 ||
+      (flags & MOON_DISPATCH_FUSED_DUPS && flags & MOON_DISPATCH_DEDUP_EPILOGUE))
+    return MOON_ERR_INVALID_ARG;
   void* hout = hidden_out != nullptr ? hidden_out : ctx->hidden_win;
   float* wout = weights_out != nullptr ? weights_out : ctx->w_win;
   if (!aligned(hidden_rsh, 16) || !aligned(hout, 16) || !aligned(weights_rsk, 4) ||
@@ -384,7 +389,7 @@ moon_status moon_dispatch(moon_ctx* ctx, const moon_comm_plan* plan, const void*
   DeviceGuard g(ctx->device);
   if (moon::launch_dispatch(ctx->d, plan->a, static_cast<const uint16_t*>(hidden_rsh), weights_rsk,
                             static_cast<uint16_t*>(hout), wout,
-                            (flags & MOON_DISPATCH_FUSED_DUPS) != 0, stream) != hipSuccess)
+                            (flags & MOON_DISPATCH_DEDUP_EPILOGUE) != 0, stream) != hipSuccess)
     return MOON_ERR_HIP;
   return MOON_OK;
 }

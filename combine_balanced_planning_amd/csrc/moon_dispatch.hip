@@ -6,23 +6,28 @@
 //  rank fills the duplicate routes from their primary row.)
 //
 // The rank windows are one HBM array, so the remote store of the pages is a
-// scatter of 16-byte vectors.  Bound: HBM bandwidth.
+// scatter of 16-byte vectors.  Bound: HBM bandwidth, and about nine tenths
+// of the bytes are writes to scattered rows.
 //
-//   k_dispatch_scatter  persistent grid; a work item is one wave on a 7 KB
-//                       slice (448 vectors; a row of up to 7 KB is one item)
-//                       of one token's row, read once with plain loads and
-//                       stored with non-temporal stores to each primary row
-//                       of the token (cached stores for primaries the
-//                       epilogue re-reads, when all such rows
-//                       fit in a budget of the last-level cache); slice 0 also
-//                       scatters the K route weights.  Further items zero the
-//                       padding rows of a rank's home-expert and slot groups
-//                       (the only ones that can hold rows), two rows each.
-//   k_dispatch_expand   persistent grid; a work item is one wave on a 4 KB
-//                       slice of one duplicate group's primary row (plain
-//                       loads where the scatter kept the primaries in the
-//                       caches, non-temporal ones otherwise); the lanes also
-//                       fetch the group's duplicate row offsets, then the
+//   k_dispatch_scatter<FUSED=true>   (the default) persistent grid; a work
+//                       item is one wave on a 2 KB slice (128 vectors) of one
+//                       token's row, read once with plain loads and stored
+//                       with non-temporal stores to the rows of all K routes
+//                       (primaries and duplicates alike: a duplicate row gets
+//                       the same bits from registers, so no second pass reads
+//                       the primary back); slice 0 also scatters the K route
+//                       weights.  Further items zero the padding rows of a
+//                       rank's home-expert and slot groups (the only ones that
+//                       can hold rows), two rows each.
+//   k_dispatch_scatter<FUSED=false>  the pages' structure: as above on 7 KB
+//                       slices, but only primary rows are stored (through the
+//                       caches for primaries the epilogue re-reads, when all
+//                       such rows fit in a budget of the last-level cache);
+//   k_dispatch_expand   then the epilogue: persistent grid; a work item is one
+//                       wave on a 4 KB slice of one duplicate group's primary
+//                       row (plain loads where the scatter kept the primaries
+//                       in the caches, non-temporal ones otherwise); the lanes
+//                       also fetch the group's duplicate row offsets, then the
 //                       slice is stored to each duplicate row.
 //
 // All copies move bits; no floating-point arithmetic is done.
@@ -33,12 +38,15 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWavesPerBlock * kWave;
-// 16-byte vectors per lane in a scatter slice.  Measured (dispatch µs,
-// widths 2 / 4 / 7 / 8 / 14): r8-e64-k6 94.8 / 87.1 / 86.0 / 85.9 / 86.3,
-// where 7 makes a 4 KB row one item; DSv3 shape 1044 / 1056 / 1048 / 1051 /
-// 1069; R=16 shape 3880 / 4306 / 3875 / 3886 / 3874, where 4 leaves the
-// last of four slices of a 14 KB row half empty.
+// 16-byte vectors per lane in a scatter slice.  Primaries only (the
+// epilogue path), measured dispatch µs for widths 2 / 4 / 7 / 8 / 14:
+// r8-e64-k6 94.8 / 87.1 / 86.0 / 85.9 / 86.3, where 7 makes a 4 KB row one
+// item; DSv3 shape 1044 / 1056 / 1048 / 1051 / 1069; R=16 shape 3880 / 4306
+// / 3875 / 3886 / 3874, where 4 leaves the last of four slices of a 14 KB row
+// half empty.
 constexpr int kSliceVec = 7;
+// The same for the fused scatter, which stores each slice K times.
+constexpr int kFusedSliceVec = 2;
 // Padding rows per zero-fill item (a sweep of 1, 2, 4, 8, 16: 2 is 5 % faster
 // than 8 at serving decode, where padding dominates, and equal elsewhere).
 constexpr int kZeroRows = 2;
@@ -50,16 +58,21 @@ constexpr int64_t kKeepBudgetBytes = 128ll << 20;
 constexpr int kExpandSliceVec = 4;  // 16-byte vectors per lane in an epilogue slice
 constexpr int kExpandUnroll = 1;    // epilogue items a wave has in flight
 
+// SV: vectors per lane in a slice.  FUSED: store the slice to every route's
+// row (slice-major: for each of the lane's vectors, the K rows in turn);
+// else to primary rows only (route-major), caching the primaries that the
+// epilogue reads back when `keep_dup_primaries`.
+template <int SV, bool FUSED>
 __global__ void __launch_bounds__(kThreads)
     k_dispatch_scatter(Dims d, PlanArrays pa, const u32x4* __restrict__ hidden,
                        const float* __restrict__ w, u32x4* __restrict__ win,
-                       float* __restrict__ wwin, int fused, int keep_dup_primaries) {
+                       float* __restrict__ wwin, int keep_dup_primaries) {
   // The plan's status is checked before the first store of each work item;
   // the item's loads do not depend on it, so they overlap with its load.
   const int status = pa.status[0];
   const int lane = threadIdx.x & (kWave - 1);
   const int V = d.H / 8;
-  const int nsl = (V + kWave * kSliceVec - 1) / (kWave * kSliceVec);
+  const int nsl = (V + kWave * SV - 1) / (kWave * SV);
   const int64_t tok_items = (int64_t)d.R * d.S * nsl;
   const int zpg = (d.P - 1 + kZeroRows - 1) / kZeroRows;  // zero items per group
   // Only a rank's own E/R home experts and its B slots can hold rows: the
@@ -77,17 +90,28 @@ __global__ void __launch_bounds__(kThreads)
       const bool wlane = lane < d.K && w != nullptr && sl == 0;
       if (lane < d.K) dl = pa.dst[t * d.K + lane];
       if (wlane) wk = w[t * d.K + lane];
-      const int c0 = sl * kWave * kSliceVec;
+      const int c0 = sl * kWave * SV;
       const u32x4* src = hidden + t * V;
-      u32x4 buf[kSliceVec];
+      u32x4 buf[SV];
       // (non-temporal loads: 1 % slower at the DSv3 and R=16 shapes)
 #pragma unroll
-      for (int c = 0; c < kSliceVec; ++c) {
+      for (int c = 0; c < SV; ++c) {
         const int j = c0 + c * kWave + lane;
         if (j < V) buf[c] = src[j];
       }
       if (status != 0) return;
       if (wlane) wwin[dst_global_row(dl)] = wk;
+      if (FUSED) {
+#pragma unroll
+        for (int c = 0; c < SV; ++c) {
+          const int j = c0 + c * kWave + lane;
+          for (int k = 0; k < d.K; ++k) {
+            u32x4* dp = win + dst_global_row(__builtin_amdgcn_readlane(dl, k)) * V;
+            if (j < V) __builtin_nontemporal_store(buf[c], dp + j);
+          }
+        }
+        continue;
+      }
       // Lanes k whose primary row the epilogue will read back (a later route
       // of the token goes to the same rank): stored through the caches when
       // the host judged that such rows fit in the last-level cache.
@@ -104,17 +128,17 @@ __global__ void __launch_bounds__(kThreads)
       }
       for (int k = 0; k < d.K; ++k) {
         const int dk = __builtin_amdgcn_readlane(dl, k);
-        if (dk < 0 && !fused) continue;  // duplicate: written by the epilogue
-        u32x4* dp = win + dst_global_row(dk) * V;
+        if (dk < 0) continue;  // duplicate: written by the epilogue
+        u32x4* dp = win + (int64_t)dk * V;
         if ((keep >> k) & 1) {
 #pragma unroll
-          for (int c = 0; c < kSliceVec; ++c) {
+          for (int c = 0; c < SV; ++c) {
             const int j = c0 + c * kWave + lane;
             if (j < V) dp[j] = buf[c];
           }
         } else {
 #pragma unroll
-          for (int c = 0; c < kSliceVec; ++c) {
+          for (int c = 0; c < SV; ++c) {
             const int j = c0 + c * kWave + lane;
             if (j < V) __builtin_nontemporal_store(buf[c], dp + j);
           }
@@ -208,26 +232,41 @@ __global__ void __launch_bounds__(kThreads) k_dispatch_expand(Dims d, PlanArrays
   }
 }
 
-}  // namespace
-
-hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* hidden,
-                           const float* w, uint16_t* win, float* wwin, bool fused, hipStream_t s) {
+// Persistent scatter grid: enough 4-wave workgroups for every item, at most
+// kScatterBlocks.
+template <int SV>
+int scatter_blocks(const Dims& d) {
   const int V = d.H / 8;
-  const int nsl = (V + kWave * kSliceVec - 1) / (kWave * kSliceVec);
+  const int nsl = (V + kWave * SV - 1) / (kWave * SV);
   const int zpg = (d.P - 1 + kZeroRows - 1) / kZeroRows;
   const int64_t items = (int64_t)d.R * d.S * nsl + (int64_t)d.R * (d.Eg + d.B) * zpg;
   const int64_t want = (items + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int blocks = (int)(want < kScatterBlocks ? (want > 0 ? want : 1) : kScatterBlocks);
+  return (int)(want < kScatterBlocks ? (want > 0 ? want : 1) : kScatterBlocks);
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* hidden,
+                           const float* w, uint16_t* win, float* wwin, bool epilogue,
+                           hipStream_t s) {
+  const auto* hv = reinterpret_cast<const u32x4*>(hidden);
+  auto* wv = reinterpret_cast<u32x4*>(win);
+  if (!epilogue || d.K == 1) {
+    hipLaunchKernelGGL((k_dispatch_scatter<kFusedSliceVec, true>),
+                       dim3(scatter_blocks<kFusedSliceVec>(d)), dim3(kThreads), 0, s, d, pa, hv, w,
+                       wv, wwin, 0);
+    return hipGetLastError();
+  }
   // The epilogue re-reads one primary row per duplicate group (about 1.3
   // per token on uniform routing).  When the call's token rows fit a budget
   // of the last-level cache, the scatter stores those primaries through the
   // caches so the epilogue can find them there.
-  const int keep = !fused && d.K > 1 && (int64_t)d.R * d.S * d.H * 2 <= kKeepBudgetBytes;
-  hipLaunchKernelGGL(k_dispatch_scatter, dim3(blocks), dim3(kThreads), 0, s, d, pa,
-                     reinterpret_cast<const u32x4*>(hidden), w, reinterpret_cast<u32x4*>(win),
-                     wwin, fused ? 1 : 0, keep);
+  const int V = d.H / 8;
+  const int keep = (int64_t)d.R * d.S * d.H * 2 <= kKeepBudgetBytes;
+  hipLaunchKernelGGL((k_dispatch_scatter<kSliceVec, false>), dim3(scatter_blocks<kSliceVec>(d)),
+                     dim3(kThreads), 0, s, d, pa, hv, w, wv, wwin, keep);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || fused || d.K == 1) return e;
+  if (e != hipSuccess) return e;
   // The group count is only known on the device; size the persistent grid by
   // its bound R*S*(K/2) (a token has at most K/2 groups), times the slices.
   constexpr int SW = kWave * kExpandSliceVec;
@@ -240,10 +279,10 @@ hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* 
   // slower where the primaries are kept).
   if (keep)
     hipLaunchKernelGGL((k_dispatch_expand<kExpandSliceVec, kExpandUnroll, false>), dim3(eblocks),
-                       dim3(kThreads), 0, s, d, pa, reinterpret_cast<u32x4*>(win));
+                       dim3(kThreads), 0, s, d, pa, wv);
   else
     hipLaunchKernelGGL((k_dispatch_expand<kExpandSliceVec, kExpandUnroll, true>), dim3(eblocks),
-                       dim3(kThreads), 0, s, d, pa, reinterpret_cast<u32x4*>(win));
+                       dim3(kThreads), 0, s, d, pa, wv);
   return hipGetLastError();
 }
 

@@ -60,9 +60,10 @@ __device__ __forceinline__ uint64_t pack_word(uint32_t tag, uint32_t a, uint32_t
   return ((uint64_t)(tag & 0xFFFFu) << 48) | ((uint64_t)(a & 0xFFFFFFu) << 24) | (b & 0xFFFFFFu);
 }
 
-// Plan arrays (one allocation).
+// Plan arrays (one allocation).  pidx [R,B,2]: (owner rank, rank-local row)
+// of each slot's expert, (-1,-1) for an unused slot.
 struct PlanArrays {
-  int32_t *dst, *etc, *zfr, *rstats, *dup_groups, *dup_loffs, *dup_counts, *cu, *status;
+  int32_t *dst, *etc, *zfr, *rstats, *dup_groups, *dup_loffs, *dup_counts, *cu, *status, *pidx;
 };
 
 }  // namespace moon
@@ -91,8 +92,11 @@ namespace moon {
 // Kernel launchers (each returns a hipError_t from the launch).
 hipError_t launch_plan(const Dims& d, const Scratch& sc, const PlanArrays& pa, const int32_t* topk,
                        const int32_t* tpe, hipStream_t s);
+// epilogue: scatter primaries, then expand duplicates in a second kernel
+// (else every route's row is stored by the scatter).
 hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* hidden,
-                           const float* w, uint16_t* win, float* wwin, bool fused, hipStream_t s);
+                           const float* w, uint16_t* win, float* wwin, bool epilogue,
+                           hipStream_t s);
 // fold != NULL selects the duplicate prologue; folded primary rows are
 // written there ([R*NvS, H], the context window).
 hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y,

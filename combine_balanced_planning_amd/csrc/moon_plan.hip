@@ -22,7 +22,8 @@
 //                     the alias fill over the R rank loads (one wave, one lane
 //                     per rank), then per rank its slots and the start rows of
 //                     its padded groups; tile u also writes rank u's
-//                     experts_to_copy, remote_stats, cu_seqlens and
+//                     experts_to_copy (with each slot's owner rank and row,
+//                     the prefetch index), remote_stats, cu_seqlens and
 //                     zero_fill_ranges;
 //                   - placement: stable rank of every route = tile base + wave
 //                     prefix + running per-wave counter + rank inside the chunk
@@ -119,12 +120,17 @@ __global__ void __launch_bounds__(kPlanThreads)
   int bad = 0;
   for (int64_t i = i0 + threadIdx.x; i < i1; i += 8 * kPlanThreads) {
     int e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = i + j * kPlanThreads < i1 ? topk[i + j * kPlanThreads] : -2;
+    bool in[8];  // the slot holds a route of the tile (every id value is checked)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      in[j] = i + j * kPlanThreads < i1;
+      e[j] = in[j] ? topk[i + j * kPlanThreads] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!in[j]) continue;
       if ((unsigned)e[j] < (unsigned)E) atomicAdd(&cnt[e[j]], 1);
-      else if (e[j] != -2) bad = 1;
+      else bad = 1;
     }
   }
   if (bad) atomicOr(&sBad, 1);
@@ -386,6 +392,8 @@ __device__ __forceinline__ void rank_layout(const Dims& d, const PlanArrays& pa,
     if (j < Eg) L.sst[u * Eg + j] = kept ? end - pad : -1;
     if (writer && kept) {
       pa.etc[u * B + slot] = o * Eg + j;
+      pa.pidx[(u * B + slot) * 2 + 0] = o;  // owner rank and row of the expert
+      pa.pidx[(u * B + slot) * 2 + 1] = j;
       cu[E + slot] = end;
       zfr[(E + slot) * 2 + 0] = end - pad + n;
       zfr[(E + slot) * 2 + 1] = end;
@@ -401,6 +409,8 @@ __device__ __forceinline__ void rank_layout(const Dims& d, const PlanArrays& pa,
     const int used = min(count, B);
     for (int j = used + lane; j < B; j += kWave) {
       pa.etc[u * B + j] = -1;
+      pa.pidx[(u * B + j) * 2 + 0] = -1;
+      pa.pidx[(u * B + j) * 2 + 1] = -1;
       cu[E + j] = carry;
       zfr[(E + j) * 2 + 0] = carry;
       zfr[(E + j) * 2 + 1] = carry;

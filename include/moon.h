@@ -76,9 +76,15 @@ typedef enum {
  * and skips duplicates.  The window's dispatched rows at those primaries are
  * overwritten. */
 #define MOON_COMBINE_DUP_PROLOGUE 0x4u
-/* Dispatch flag: write duplicate rows from registers in the scatter kernel
- * instead of expanding them in the epilogue (same result). */
+/* Dispatch flags.  By default the scatter stores every route's row,
+ * duplicates included, from registers (one pass; MOON_DISPATCH_FUSED_DUPS
+ * names this default explicitly).  MOON_DISPATCH_DEDUP_EPILOGUE selects the
+ * pages' two-pass structure (Guide, Buffer.dispatch): the scatter stores each
+ * token's primary row once per destination rank, then an epilogue on the
+ * receiving rank copies every primary into its duplicate rows.  Both give
+ * the same windows; the two flags together are rejected. */
 #define MOON_DISPATCH_FUSED_DUPS 0x2u
+#define MOON_DISPATCH_DEDUP_EPILOGUE 0x8u
 
 /* Constructor controls (Guide, Buffer(...)): R = number of EP ranks,
  * B <= 0 selects the default E/R, token_padding = alignment in rows of every
@@ -104,11 +110,17 @@ typedef struct {
  * (slots used, routes placed in slots), dup_groups [R,NvS,3] (primary local
  * row, first dup_loffs index, count), dup_loffs [R,NvS], dup_counts [R,2]
  * (valid prefix sizes), cu_seqlens [R,E+B] (inclusive padded end offsets),
- * status [1] (internal error bits). */
+ * status [1] (internal error bits), and one array the planner adds beside
+ * the pages' fields: prefetch_index [R,B,2], for every (rank, slot) the
+ * (owner rank, rank-local expert row) of experts_to_copy, or (-1,-1) for an
+ * unused slot: the split of the expert id that Buffer.prefetch_weight
+ * performs before its copy (written by moon_plan; moon_prefetch_index
+ * computes the same into a caller's array). */
 typedef struct {
   int32_t *dst, *experts_to_copy, *zero_fill_ranges, *remote_stats, *dup_groups, *dup_loffs,
       *dup_counts, *cu_seqlens, *status;
   int32_t N, R, E, B, NvS, K;
+  int32_t* prefetch_index;
 } moon_plan_arrays;
 
 typedef struct moon_ctx moon_ctx;
@@ -158,11 +170,13 @@ moon_status moon_plan(moon_ctx* ctx, const int32_t* topk_rsk, const int32_t* tok
 /* Dispatch with a plan (Guide, Buffer.dispatch): hidden_rsh [R,S,H] bf16
  * token rows are copied once per destination rank to their primary rows,
  * weights_rsk [R,S,K] fp32 (optional) go to every route's row, padding rows
- * are zeroed, then duplicate rows are expanded from their primaries.
+ * are zeroed; duplicate rows receive the same bits as their primaries (see
+ * the dispatch flags).
  * hidden_out / weights_out: [R*NvS,H] bf16 / [R*NvS] fp32, or NULL for the
  * context windows.  Rows after a rank's last group are not written.  Passing
  * an existing plan again is the backward path (Guide: planning is skipped).
- * flags: 0 or MOON_DISPATCH_FUSED_DUPS. */
+ * flags: 0, MOON_DISPATCH_FUSED_DUPS (the same as 0) or
+ * MOON_DISPATCH_DEDUP_EPILOGUE. */
 moon_status moon_dispatch(moon_ctx* ctx, const moon_comm_plan* plan, const void* hidden_rsh,
                           const float* weights_rsk, void* hidden_out, float* weights_out,
                           uint32_t flags, hipStream_t stream);

@@ -42,6 +42,9 @@ def compare_plan(got, ref):
             bad = np.argwhere(g != e)[:5]
             raise AssertionError(f"plan field {f} differs at {bad.tolist()}: "
                                  f"{g[tuple(bad[0])]} vs {e[tuple(bad[0])]}")
+    if "prefetch_index" in got:  # the planner's split of experts_to_copy
+        assert np.array_equal(got["prefetch_index"], oracle.prefetch_index(ref)), \
+            "plan prefetch_index differs from the oracle's prefetch index"
     for r in range(ref.R):
         ng, nd = ref.dup_counts[r]
         assert np.array_equal(got["dup_groups"][r, :ng], ref.dup_groups[r, :ng]), \

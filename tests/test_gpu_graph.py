@@ -67,6 +67,7 @@ def test_graph_replay_matches_eager(config):
         for k in ("dst", "zero_fill_ranges", "remote_stats", "dup_counts", "cu_seqlens"):
             pt_[k].zero_()
         pt_["experts_to_copy"].fill_(-1)
+        pt_["prefetch_index"].fill_(-7)
         pt_["status"].fill_(8)
 
     try:

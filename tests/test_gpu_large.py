@@ -1,11 +1,19 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark uses.
 
-The whole plan (dst, layout, slots, duplicate records) is compared bit for
-bit with the oracle.  Windows and combine outputs are compared on samples the
-oracle computes one by one: bulk inputs are filled on the GPU by the seeded
-generator and the needed rows are regenerated on the host (the fill itself is
-checked against the host generator first).
+The whole plan (dst, layout, slots, duplicate records, prefetch index) is
+compared bit for bit with the oracle.  Bulk inputs are filled on the GPU by
+the seeded generator (the fill itself is checked against the host generator
+first) and the rows a comparison needs are regenerated on the host:
+
+* DSv3 shape: every covered row of every rank window (routed rows against
+  their token's row, padding rows against zero) and the weight windows in
+  full, for the default one-pass dispatch and for the pages' two-pass
+  structure (whose epilogue reads the primaries with non-temporal loads at
+  this size); combine over every token of one source rank.
+* R=16 shape at maxvio 8: the window of the rank with the most slots in
+  full, for both dispatch paths, and combine over every token of one source
+  rank; the other maxvio levels on sampled rows and tokens.
 """
 import numpy as np
 import pytest
@@ -52,43 +60,49 @@ def sample_rows(rng, ref, src, n_routes=2048, n_groups=4):
     return np.array(sorted(rows), np.int64)
 
 
-@pytest.mark.parametrize("config,level", [("dsv3", 0), ("r16-e384-k8", 0),
-                                          ("r16-e384-k8", 2), ("r16-e384-k8", 4)])
-def test_full_size_sampled_parity(env, config, level):
-    import torch
+class Run:
+    """Plan + dispatch + combine of one full-size workload on the GPU, and the
+    oracle's plan of the same routing (compared bit for bit)."""
 
-    import synth.gpu as sg
-    moon, dev = env
-    wl = synth.workload(config, level)
-    R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
-    seed = wl["seed"]
-    say(f"[case] {wl['name']} level {level} maxvio={wl['maxvio']:.3f} R={R} E={E} K={K} "
-        f"S={S} H={H}")
-    rng = np.random.default_rng(seed)
-    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
-    plan = moon.moon_plan_create(ctx)
-    try:
+    def __init__(self, moon, dev, config, level, dflags):
+        import torch
+
+        import synth.gpu as sg
+        wl = synth.workload(config, level)
+        self.wl = wl
+        R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+        self.R, self.E, self.K, self.S, self.H = R, E, K, S, H
+        seed = wl["seed"]
+        say(f"[case] {wl['name']} level {level} maxvio={wl['maxvio']:.3f} R={R} E={E} K={K} "
+            f"S={S} H={H} dflags={dflags}")
+        self.ctx = ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+        self.plan = plan = moon.moon_plan_create(ctx)
         NvS = ctx.NvS
-        hidden = sg.hidden(seed, R, S, H, dev)
-        y = sg.y(seed, R * NvS, H, dev)
+        self.hidden = sg.hidden(seed, R, S, H, dev)
+        self.y = sg.y(seed, R * NvS, H, dev)
+        self.kh = synth.stream_key(seed, synth.TAG_HIDDEN)
+        self.ky = synth.stream_key(seed, synth.TAG_Y)
+        rng = np.random.default_rng(seed)
+        self.rng = rng
         # the GPU fill is the host generator, bit for bit
-        kh, ky = synth.stream_key(seed, synth.TAG_HIDDEN), synth.stream_key(seed, synth.TAG_Y)
         probe = np.array([0, 1, R * S - 1, int(rng.integers(R * S))])
-        assert np.array_equal(pt.dev_bits(hidden.view(R * S, H)[torch.from_numpy(probe).to(dev)]),
-                              synth.bf16_rows(kh, probe, H))
+        assert np.array_equal(
+            pt.dev_bits(self.hidden.view(R * S, H)[torch.from_numpy(probe).to(dev)]),
+            synth.bf16_rows(self.kh, probe, H))
         w_d = pt.to_dev(wl["w"], dev)
         moon.moon_plan(ctx, pt.to_dev(wl["topk"], dev), None, plan)
-        moon.moon_dispatch(ctx, plan, hidden, w_d)
-        win, wwin = moon.window_tensors(ctx)
-        out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
-        wsk = torch.empty((R, S, K), dtype=torch.float32, device=dev)
-        moon.moon_combine(ctx, plan, y, wwin, moon.MOON_COMBINE_WEIGHTED, out, wsk)
-        pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
-        moon.moon_prefetch_index(ctx, plan, pidx)
+        moon.moon_dispatch(ctx, plan, self.hidden, w_d, flags=dflags)
+        self.win, self.wwin = moon.window_tensors(ctx)
+        self.out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
+        self.wsk = torch.empty((R, S, K), dtype=torch.float32, device=dev)
+        moon.moon_combine(ctx, plan, self.y, self.wwin, moon.MOON_COMBINE_WEIGHTED, self.out,
+                          self.wsk)
+        self.pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
+        moon.moon_prefetch_index(ctx, plan, self.pidx)
         assert moon.moon_plan_status(plan) == moon.MOON_OK
         got = pt.gpu_plan_arrays(plan)
 
-        ref = oracle.plan(wl["topk"], E, B, P)
+        self.ref = ref = oracle.plan(wl["topk"], E, B, P)
         assert ref.status == oracle.OK
         pt.compare_plan(got, ref)
         pv = pt.gpu_plan_view(got, ref)
@@ -97,39 +111,132 @@ def test_full_size_sampled_parity(env, config, level):
         pc.check_slots(pv)
         say(f"   plan bit-exact; slots used {int(ref.remote_stats[:, 0].sum())}, "
             f"dup rows {int(ref.dup_counts[:, 1].sum())}")
-        assert np.array_equal(pidx.cpu().numpy(), oracle.prefetch_index(ref))
+        assert np.array_equal(self.pidx.cpu().numpy(), oracle.prefetch_index(ref))
+        self.src = oracle.row_sources(ref)
+        _, self.ewwin = oracle.dispatch(ref, np.zeros((R, S, 0), np.uint16), wl["w"])
+        # every covered weight-window entry, bit for bit
+        cov = self.src != -2
+        assert np.array_equal(self.wwin.cpu().numpy()[cov].view(np.uint32),
+                              self.ewwin[cov].view(np.uint32)), "weight windows differ"
 
-        # dispatch: sampled rows against the regenerated source rows
-        src = oracle.row_sources(ref)
-        _, ewwin = oracle.dispatch(ref, np.zeros((R, S, 0), np.uint16), wl["w"])
-        rows = sample_rows(rng, ref, src)
-        rows_d = torch.from_numpy(rows).to(dev)
-        g_rows = pt.dev_bits(win[rows_d])
-        g_w = wwin[rows_d].cpu().numpy()
-        s = src[rows]
+    def close(self, moon):
+        moon.moon_plan_destroy(self.plan)
+        moon.moon_ctx_destroy(self.ctx)
+
+    def check_window(self, u, hidden_host):
+        """Every covered row of rank u's window: routed rows equal their
+        token's row, padding rows are zero."""
+        NvS, H, K = self.ctx.NvS, self.H, self.K
+        g = pt.dev_bits(self.win[u * NvS:(u + 1) * NvS])
+        s = self.src[u * NvS:(u + 1) * NvS]
+        routed, pad = s >= 0, s == -1
+        assert np.array_equal(g[routed], hidden_host[s[routed] // K]), \
+            f"routed rows of rank {u} differ"
+        assert not g[pad].any(), f"padding rows of rank {u} are not zero"
+        return int(routed.sum()), int(pad.sum())
+
+    def check_rows(self, rows):
+        """Sampled window rows against the regenerated source rows."""
+        import torch
+        H, K = self.H, self.K
+        rows_d = torch.from_numpy(rows).to(self.win.device)
+        g_rows = pt.dev_bits(self.win[rows_d])
+        s = self.src[rows]
         routed = s >= 0
         exp = np.zeros((rows.shape[0], H), np.uint16)
-        exp[routed] = synth.bf16_rows(kh, s[routed] // K, H)
+        exp[routed] = synth.bf16_rows(self.kh, s[routed] // K, H)
         cov = s != -2
         assert np.array_equal(g_rows[cov], exp[cov]), "sampled window rows differ"
-        assert np.array_equal(g_w[cov].view(np.uint32), ewwin[rows][cov].view(np.uint32))
-        say(f"   {int(cov.sum())} window rows ({int((s == -1).sum())} padding) bit-exact")
+        return int(cov.sum())
 
-        # combine: sampled tokens, the oracle on regenerated rows
-        toks = np.unique(np.concatenate([rng.choice(R * S, 384, replace=False),
-                                         [0, R * S - 1]]))
-        dst_tok = ref.dst.reshape(R * S, K)[toks]
+    def check_combine(self, toks):
+        """Combine outputs and gathered weights of tokens `toks` (global token
+        ids) against the oracle on regenerated rows."""
+        import torch
+        R, S, K, H = self.R, self.S, self.K, self.H
+        dst_tok = self.ref.dst.reshape(R * S, K)[toks]
         need = np.unique(pc.decode(dst_tok).reshape(-1))
-        yrows = synth.bf16_rows(ky, need, H)
-        eout, ewsk, acc = oracle.combine_rows(dst_tok, need, yrows, ewwin[need], weighted=True)
-        toks_d = torch.from_numpy(toks).to(dev)
-        g_out = pt.dev_bits(out.view(R * S, H)[toks_d])
-        absum = pt.abs_sum(dst_tok, need, yrows, ewwin[need], True)
+        yrows = synth.bf16_rows(self.ky, need, H)
+        eout, ewsk, acc = oracle.combine_rows(dst_tok, need, yrows, self.ewwin[need],
+                                              weighted=True)
+        toks_d = torch.from_numpy(toks).to(self.out.device)
+        g_out = pt.dev_bits(self.out.view(R * S, H)[toks_d])
+        absum = pt.abs_sum(dst_tok, need, yrows, self.ewwin[need], True)
         dmax, ndiff = pt.check_combine(g_out, eout, acc, absum, K)
-        assert np.array_equal(wsk.view(R * S, K)[toks_d].cpu().numpy().view(np.uint32),
+        assert np.array_equal(self.wsk.view(R * S, K)[toks_d].cpu().numpy().view(np.uint32),
                               ewsk.view(np.uint32))
-        say(f"   combine on {toks.shape[0]} tokens: max|d|={dmax:.3g}, "
-            f"bf16 mismatches {ndiff}/{g_out.size}")
+        return dmax, ndiff, g_out.size
+
+
+def _flags(moon, path):
+    return moon.MOON_DISPATCH_DEDUP_EPILOGUE if path == "epilogue" else 0
+
+
+@pytest.mark.parametrize("path", ["fused", "epilogue"])
+def test_dsv3_every_window_row(env, path):
+    """DSv3 shape: all eight rank windows compared row for row; combine over
+    every token of source rank 3."""
+    moon, dev = env
+    run = Run(moon, dev, "dsv3", 0, _flags(moon, path))
+    try:
+        hidden_host = synth.hidden_bf16(run.wl["seed"], run.R, run.S, run.H).reshape(
+            run.R * run.S, run.H)
+        tot_r = tot_p = 0
+        for u in range(run.R):
+            r, p = run.check_window(u, hidden_host)
+            tot_r, tot_p = tot_r + r, tot_p + p
+        say(f"   all windows bit-exact: {tot_r} routed rows, {tot_p} padding rows")
+        del hidden_host
+        toks = np.arange(3 * run.S, 4 * run.S)
+        dmax, ndiff, n = run.check_combine(toks)
+        say(f"   combine on rank 3's {toks.shape[0]} tokens: max|d|={dmax:.3g}, "
+            f"bf16 mismatches {ndiff}/{n}")
     finally:
-        moon.moon_plan_destroy(plan)
-        moon.moon_ctx_destroy(ctx)
+        run.close(moon)
+
+
+@pytest.mark.parametrize("path", ["fused", "epilogue"])
+def test_r16_maxvio8_busiest_window(env, path):
+    """R=16 shape at maxvio 8 (half the tokens inside one home rank): the
+    window of the rank with the most slots compared row for row, then a
+    sample of the others; combine over every token of source rank 0."""
+    moon, dev = env
+    run = Run(moon, dev, "r16-e384-k8", 4, _flags(moon, path))
+    try:
+        u = int(np.argmax(run.ref.remote_stats[:, 0]))
+        NvS, K = run.ctx.NvS, run.K
+        s = run.src[u * NvS:(u + 1) * NvS]
+        toks = np.unique(s[s >= 0] // K)  # tokens routed to rank u
+        rows = synth.bf16_rows(run.kh, toks, run.H)
+        hidden_host = np.zeros((run.R * run.S, run.H), np.uint16)
+        hidden_host[toks] = rows
+        del rows
+        r, p = run.check_window(u, hidden_host)
+        del hidden_host
+        say(f"   rank {u} ({int(run.ref.remote_stats[u, 0])} slots): {r} routed rows from "
+            f"{toks.shape[0]} tokens, {p} padding rows bit-exact")
+        n = run.check_rows(sample_rows(run.rng, run.ref, run.src))
+        say(f"   {n} sampled rows of all ranks bit-exact")
+        toks = np.arange(0, run.S)
+        dmax, ndiff, n = run.check_combine(toks)
+        say(f"   combine on rank 0's {toks.shape[0]} tokens: max|d|={dmax:.3g}, "
+            f"bf16 mismatches {ndiff}/{n}")
+    finally:
+        run.close(moon)
+
+
+@pytest.mark.parametrize("level", [0, 2])
+def test_r16_other_levels_sampled(env, level):
+    """R=16 shape at maxvio about 0 and 2: plan in full, sampled window rows
+    and combine tokens."""
+    moon, dev = env
+    run = Run(moon, dev, "r16-e384-k8", level, 0)
+    try:
+        n = run.check_rows(sample_rows(run.rng, run.ref, run.src))
+        say(f"   {n} sampled window rows bit-exact")
+        toks = np.unique(np.concatenate([run.rng.choice(run.R * run.S, 384, replace=False),
+                                         [0, run.R * run.S - 1]]))
+        dmax, ndiff, n = run.check_combine(toks)
+        say(f"   combine on {toks.shape[0]} tokens: max|d|={dmax:.3g}, bf16 mismatches {ndiff}/{n}")
+    finally:
+        run.close(moon)

@@ -95,12 +95,17 @@ def workload_inputs(config, level=0):
 
 @pytest.mark.parametrize("config,level", [("tiny", 0), ("r8-e64-k6", 0)] +
                          [("r8-e64-k6-skewed", lv) for lv in range(4)])
-def test_workload_full_parity(env, config, level):
+@pytest.mark.parametrize("path", ["fused", "epilogue"])
+def test_workload_full_parity(env, config, level, path):
+    """The default one-pass dispatch and the pages' two-pass (epilogue)
+    structure, each against the oracle in full."""
     moon, dev = env
     wl, hidden, y = workload_inputs(config, level)
-    say(f"[workload] {wl['name']} level {level} maxvio={wl['maxvio']:.3f}")
+    say(f"[workload] {wl['name']} level {level} maxvio={wl['maxvio']:.3f} {path}")
     run_full(moon, dev, wl["topk"], wl["w"], hidden, y, wl["R"], wl["E"], wl["K"], wl["S"],
-             wl["H"], wl["B"], wl["P"], label=wl["name"])
+             wl["H"], wl["B"], wl["P"], label=wl["name"],
+             dflags=moon.MOON_DISPATCH_DEDUP_EPILOGUE if path == "epilogue" else 0,
+             weighted=path == "fused" or level % 2 == 0)
 
 
 def _edge_topk(rng, R, S, K, E, mode):
@@ -151,8 +156,9 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("path", ["fused", "epilogue"])
 @pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
-def test_edge_shapes(env, case):
+def test_edge_shapes(env, case, path):
     moon, dev = env
     label, R, E, K, S, H, B, P, mode = case
     rng = np.random.default_rng(zlib.crc32(label.encode()))
@@ -164,12 +170,14 @@ def test_edge_shapes(env, case):
     w = rng.random((R, S, K)).astype(np.float32)
     hidden = synth.bf16_normal(rng.integers(1 << 62), 0, R * S * H).reshape(R, S, H)
     y = synth.bf16_normal(rng.integers(1 << 62), 0, R * ref.NvS * H).reshape(R * ref.NvS, H)
-    run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, label=label)
+    run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, label=f"{label} {path}",
+             dflags=moon.MOON_DISPATCH_DEDUP_EPILOGUE if path == "epilogue" else 0)
 
 
 def test_fused_duplicates_and_unweighted_round_trip(env):
-    """FUSED_DUPS writes the same windows; unweighted combine of the
-    dispatched windows gives K * x exactly (closed form)."""
+    """The default dispatch, the explicit FUSED_DUPS flag and the epilogue
+    flag write the same windows; unweighted combine of the dispatched windows
+    gives K * x exactly (closed form); both flags at once are refused."""
     import torch
     moon, dev = env
     wl, hidden, _ = workload_inputs("r8-e64-k6")
@@ -180,12 +188,17 @@ def test_fused_duplicates_and_unweighted_round_trip(env):
     try:
         moon.moon_plan(ctx, pt.to_dev(wl["topk"], dev), None, plan)
         h_d = pt.bf16_to_dev(hidden, dev)
-        moon.moon_dispatch(ctx, plan, h_d, None)
+        moon.moon_dispatch(ctx, plan, h_d, None, flags=moon.MOON_DISPATCH_DEDUP_EPILOGUE)
         win, _ = moon.window_tensors(ctx)
         a = win.clone()
-        win.zero_()
-        moon.moon_dispatch(ctx, plan, h_d, None, flags=moon.MOON_DISPATCH_FUSED_DUPS)
-        assert torch.equal(a.view(torch.int16), win.view(torch.int16))
+        for fl in (0, moon.MOON_DISPATCH_FUSED_DUPS):
+            win.zero_()
+            moon.moon_dispatch(ctx, plan, h_d, None, flags=fl)
+            assert torch.equal(a.view(torch.int16), win.view(torch.int16)), fl
+        with pytest.raises(moon.MoonError) as ei:
+            moon.moon_dispatch(ctx, plan, h_d, None, flags=moon.MOON_DISPATCH_FUSED_DUPS |
+                               moon.MOON_DISPATCH_DEDUP_EPILOGUE)
+        assert ei.value.status == moon.MOON_ERR_INVALID_ARG
         out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
         moon.moon_combine(ctx, plan, win, None, 0, out)
         exp = (K * h_d.float()).to(torch.bfloat16)  # K*x is exact in fp32
@@ -288,8 +301,8 @@ def test_two_contexts_on_two_streams(env):
             moon.moon_ctx_destroy(r["ctx"])
 
 
-@pytest.mark.parametrize("what", ["bad_high", "bad_negative", "histogram", "slot_budget",
-                                  "not_planned", "tpe_ok"])
+@pytest.mark.parametrize("what", ["bad_high", "bad_negative", "bad_minus2", "bad_int_min",
+                                  "histogram", "slot_budget", "not_planned", "tpe_ok"])
 def test_device_status_and_skip(env, what):
     """Data errors set the plan status; later kernels write nothing."""
     import torch
@@ -304,6 +317,12 @@ def test_device_status_and_skip(env, what):
         expect = moon.MOON_ERR_BAD_EXPERT
     elif what == "bad_negative":
         topk[0, 0, 0] = -1
+        expect = moon.MOON_ERR_BAD_EXPERT
+    elif what == "bad_minus2":
+        topk[1, 5, 0] = -2
+        expect = moon.MOON_ERR_BAD_EXPERT
+    elif what == "bad_int_min":
+        topk[0, 7, 1] = np.iinfo(np.int32).min
         expect = moon.MOON_ERR_BAD_EXPERT
     elif what in ("histogram", "tpe_ok"):
         tpe = np.stack([np.bincount(topk[r].reshape(-1), minlength=E) for r in range(R)]).astype(
@@ -492,4 +511,4 @@ def test_random_shapes(env, i):
     hidden = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * S * H).reshape(R, S, H)
     y = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * ref.NvS * H).reshape(R * ref.NvS, H)
     run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, label=f"random-{i}-{mode}",
-             weighted=bool(i % 3))
+             weighted=bool(i % 3), dflags=moon.MOON_DISPATCH_DEDUP_EPILOGUE if i % 2 else 0)
