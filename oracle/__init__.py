@@ -180,8 +180,9 @@ def row_sources(pl):
     return src
 
 
-def combine(pl, y, wnvs=None, weighted=True, H=None, lib=None):
-    """y [R*NvS,H] bf16 bits.  Returns (out [R,S,H] uint16, wsk [R,S,K] fp32, acc fp64)."""
+def combine(pl, y, wnvs=None, weighted=True, H=None, lib=None, exact=True):
+    """y [R*NvS,H] bf16 bits.  Returns (out [R,S,H] uint16, wsk [R,S,K] fp32,
+    acc fp64 -- the exact float64 sum, None when `exact` is False)."""
     lib = lib or _load()
     y = _c(y, np.uint16)
     H = y.shape[1]
@@ -189,7 +190,7 @@ def combine(pl, y, wnvs=None, weighted=True, H=None, lib=None):
     R, S, K = pl.R, pl.S, pl.K
     out = np.zeros((R, S, H), np.uint16)
     wsk = np.zeros((R, S, K), np.float32) if wnvs is not None else None
-    acc = np.zeros((R, S, H), np.float64)
+    acc = np.zeros((R, S, H), np.float64) if exact else None
     st = lib.orc_combine(R, K, S, H, pl.NvS, _p(pl.dst), _p(y), _p(wnvs), int(bool(weighted)),
                          _p(out), _p(wsk), _p(acc))
     if st != OK:

@@ -14,9 +14,9 @@
 //               (same page, Buffer.prefetch_weight)
 //   reduce    = add every slot gradient back into its expert's gradient row
 //               and clear the consumed slots (same page, Buffer.reduce_grad)
-// Arithmetic on values happens in combine (float32 in the pages' order, with
-// a float64 counterpart as the exact reference) and in the gradient reduction
-// (float32, as the pages' gradient tensors are).
+// Arithmetic on values happens in combine (float32, ascending k, with an
+// optional float64 counterpart as the exact reference) and in the gradient
+// reduction (float32, as the pages' gradient tensors are).
 
 #include "moon_oracle.h"
 
@@ -50,16 +50,19 @@ int64_t decode_row(int32_t d) { return d >= 0 ? (int64_t)d : -(int64_t)d - 1; }
 
 // One token: sum its K routed rows in ascending k, optionally scaled by the
 // route weight stored at the route's own row (Visual Guide, Buffer.combine:
-// each token's K contributions are reduced back into its row, accumulated in
-// fp32; the weights are read back through the signed dst entries, both
-// signs alike).  `out` is the fp32 sum -- each product and each addition
-// rounded to fp32 in turn, ascending k -- rounded once to bf16; `acc`
-// receives the float64 sum of the same terms, the exact reference.
+// each token's K contributions are reduced back into its row; the weights are
+// read back through the signed dst entries, both signs alike).  The pages
+// state fp32 accumulation for the duplicate prologue's fold; the main K-sum
+// is held to the same fp32 precision as the target stated for this path, and
+// its order and rounding are a reading: `out` is the fp32 sum -- each product
+// and each addition rounded to fp32 in turn, ascending k -- rounded once to
+// bf16.  When `acc` is given it receives the float64 sum of the same terms,
+// the exact reference (the fp32 result does not depend on it).
 template <class RowFn, class WFn>
 void combine_token(int32_t K, int32_t H, const int32_t* d, RowFn row, WFn wat, int32_t weighted,
                    uint16_t* out, float* wsk, double* acc) {
   std::vector<float> sum32(H, 0.0f);
-  std::vector<double> sum(H, 0.0);
+  std::vector<double> sum(acc != nullptr ? H : 0, 0.0);
   for (int k = 0; k < K; ++k) {
     int64_t G = decode_row(d[k]);
     const uint16_t* y = row(G);
@@ -70,8 +73,9 @@ void combine_token(int32_t K, int32_t H, const int32_t* d, RowFn row, WFn wat, i
       float yv = bf16_to_float(y[h]);
       float prod = c32 * yv;
       sum32[h] = sum32[h] + prod;
-      sum[h] += c * (double)yv;
     }
+    if (acc != nullptr)
+      for (int h = 0; h < H; ++h) sum[h] += c * (double)bf16_to_float(y[h]);
     if (wsk != nullptr) wsk[k] = wk;
   }
   for (int h = 0; h < H; ++h) {

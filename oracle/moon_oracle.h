@@ -78,9 +78,12 @@ int32_t orc_row_sources(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B,
 
 /* Combine over all tokens.  y [R*NvS,H] bf16 bits; wnvs [R*NvS] (needed when
  * weighted != 0).  out [R,S,H] bf16 bits: the fp32 sum of c_k * y_k, ascending
- * k, every product and addition rounded to fp32, rounded once to bf16 (the
- * pages accumulate combine in fp32).  wsk_out [R,S,K] and acc [R,S,H] (the
- * float64 sum of the same terms, the exact reference) may be NULL. */
+ * k, every product and addition rounded to fp32, rounded once to bf16 (fp32
+ * is the precision the target for this path fixes for the K-sum; the pages
+ * state fp32 for the duplicate prologue's fold only, and the order and the
+ * single rounding are a reading).  wsk_out [R,S,K] and acc [R,S,H] (the
+ * float64 sum of the same terms, the exact reference, computed only when
+ * given) may be NULL. */
 int32_t orc_combine(int32_t R, int32_t K, int32_t S, int32_t H, int32_t NvS,
                     const int32_t* dst, const uint16_t* y, const float* wnvs,
                     int32_t weighted, uint16_t* out, float* wsk_out, double* acc);

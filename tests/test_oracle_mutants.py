@@ -32,9 +32,9 @@ MUTANTS = {
     "route_weight_of_first_k": ("if (w != nullptr) wwin[G] = w[t * K + k];",
                                 "if (w != nullptr) wwin[G] = w[t * K];"),
     "combine_drops_weight": ("float c32 = weighted ? wk : 1.0f;", "float c32 = 1.0f;"),
-    "combine_fused_multiply_add": ("      sum32[h] = sum32[h] + prod;\n      sum[h] += c * (double)yv;",
-                                   "      sum32[h] = std::fma(c32, yv, sum32[h]);\n"
-                                   "      sum[h] += c * (double)yv;"),
+    "combine_fused_multiply_add": ("      sum32[h] = sum32[h] + prod;\n    }\n    if (acc != nullptr)",
+                                   "      sum32[h] = std::fma(c32, yv, sum32[h]);\n    }\n"
+                                   "    if (acc != nullptr)"),
     "combine_output_from_float64": ("    if (wsk != nullptr) wsk[k] = wk;\n  }\n  for (int h = 0; h < H; ++h) {\n"
                                     "    out[h] = orc_bf16_from_double((double)sum32[h]);",
                                     "    if (wsk != nullptr) wsk[k] = wk;\n  }\n  for (int h = 0; h < H; ++h) {\n"
