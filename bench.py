@@ -1,21 +1,27 @@
 """Benchmark of the balanced expert-parallel hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input:
-plan (histogram, balance, layout, placement, duplicate records) -> dispatch
-(scatter + zero-fill + dedup epilogue) -> combine (weighted K-sum + weight
-gather) -> prefetch index.  Inputs are resident in HBM before timing starts.
+plan (histogram, balance, layout, placement, duplicate records, prefetch
+index) -> dispatch (one-pass scatter of every route's row + weights +
+zero-fill) -> combine (weighted K-sum + weight gather).  Inputs are resident
+in HBM before timing starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload r8-e64-k6|dsv3|r16-e384-k8]
-                    [--step-only]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload r16-e384-k8|dsv3|r8-e64-k6] [--step-only]
 
-Prints one JSON line.  `value` is the dispatch+combine algorithmic HBM bytes
-of a step divided by the measured time of the whole step (plan included), in
+Prints one JSON line.  The headline workload is the largest single-GPU
+configuration (R=16, E=384, K=8, S=8192, H=7168, half of the tokens inside
+one home rank).  `value` is the dispatch+combine algorithmic HBM bytes of a
+step divided by the measured time of the whole step (plan included), in
 GB/s; the line also carries tokens/s, per-call times inside the step (HIP
-events on the stream the kernels run on), the roofline of the dominant kernel
-(its duration from back-to-back launches on the timed inputs), a maxvio sweep
-on the same shapes, the dedup ablations, weight prefetch and gradient
-reduction, the padded serving workload and the oracle timed on the host as a
-CPU baseline.  --step-only keeps just the step (the profiler runs use it).
+events on the stream the kernels run on), the roofline of the dominant
+kernel (its duration from back-to-back launches on the timed inputs), the
+memory-system ceilings of the same access patterns measured on the same
+buffers, a maxvio sweep on the same shapes, the dedup ablations, a
+secondary section on the r8-e64-k6 shape (whose data partly stays in the
+256 MB last-level cache) with weight prefetch, gradient reduction and the
+padded serving workload, and the oracle timed on the host as a CPU
+baseline.  --step-only keeps just the step (the profiler runs use it).
 """
 import argparse
 import hashlib
@@ -32,6 +38,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "dispatch+combine HBM GB/s (% of peak) and tokens/s vs maxvio; plan µs"
 PROFILES = os.path.join(ROOT, "profiles")
+HEADLINE = "r16-e384-k8"
+SECONDARY = "r8-e64-k6"
 
 
 def log(*a):
@@ -39,7 +47,8 @@ def log(*a):
 
 
 class Inputs:
-    """One batch of seeded synthetic input, resident on the GPU."""
+    """One batch of seeded synthetic input, resident on the GPU (the routing
+    also kept on the host)."""
 
     def __init__(self, moon, ctx, config, seed, alpha, dev):
         import torch
@@ -49,6 +58,8 @@ class Inputs:
         c = synth.WORKLOADS[synth.workload_id(config)]
         R, E, K, S, H = c["R"], c["E"], c["K"], c["S"], c["H"]
         topk, w = synth.routing(config, seed, alpha)
+        self.seed = seed
+        self.topk_h, self.w_h = topk, w
         self.maxvio = synth.maxvio(topk, E)
         self.topk = torch.from_numpy(topk).to(dev)
         self.w = torch.from_numpy(w).to(dev)
@@ -56,23 +67,22 @@ class Inputs:
         self.y = sg.y(seed, R * ctx.NvS, H, dev)
         self.out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
         self.wsk = torch.empty((R, S, K), dtype=torch.float32, device=dev)
-        self.pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
         self.plan = moon.moon_plan_create(ctx)
 
 
 def bytes_from_counts(R, S, K, H, n_grp, n_dup, n_pad):
     """Bytes the method must move in dispatch and combine, from a plan's
-    duplicate groups, duplicate rows and padding rows (all ranks)."""
+    duplicate groups, duplicate rows and padding rows (all ranks).
+    `dispatch` is the one-pass dispatch (every route's row written once from
+    the token's row, read once); `dispatch_epilogue` adds the epilogue's one
+    read of each duplicate group's primary row."""
     n_route = R * S * K
     row = 2 * H
     d_min = (row * R * S + row * n_route + row * n_pad + 4 * n_route * 3 + 4 * n_pad
              + 12 * n_grp + 4 * n_dup)
-    # the epilogue reads each duplicate group's primary row once and writes
-    # it to the group's duplicate rows (their writes are counted above)
-    dispatch = d_min + row * n_grp
     combine = row * n_route + row * R * S + 4 * n_route * 2 + 4 * n_route  # + weight gather
-    return dict(dispatch=dispatch, dispatch_minimal=d_min, combine=combine, n_route=n_route,
-                n_dup=n_dup, n_grp=n_grp, n_pad=n_pad)
+    return dict(dispatch=d_min, dispatch_epilogue=d_min + row * n_grp, combine=combine,
+                n_route=n_route, n_dup=n_dup, n_grp=n_grp, n_pad=n_pad)
 
 
 def plan_counts(dup_counts, zero_fill_ranges):
@@ -92,31 +102,30 @@ def algorithmic_bytes(moon, ctx, plan):
     return nb
 
 
+def step_calls(moon, ctx, s, wwin, stream, ev=None):
+    """One step: plan (with the prefetch index) -> dispatch -> combine, with
+    optional HIP events between the calls."""
+    if ev is not None:
+        ev[0].record(stream)
+    moon.moon_plan(ctx, s.topk, None, s.plan, stream=stream)
+    if ev is not None:
+        ev[1].record(stream)
+    moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream)
+    if ev is not None:
+        ev[2].record(stream)
+    moon.moon_combine(ctx, s.plan, s.y, wwin, moon.MOON_COMBINE_WEIGHTED, s.out, s.wsk,
+                      stream=stream)
+    if ev is not None:
+        ev[3].record(stream)
+
+
 def run_steps(moon, ctx, sets, steps, warmup, stream):
     """Warm up, then time exactly `steps` steps; per-call HIP events on `stream`."""
     import torch
-    win, wwin = moon.window_tensors(ctx)
-
-    def step(i, ev=None):
-        s = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
-        moon.moon_plan(ctx, s.topk, None, s.plan, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        moon.moon_combine(ctx, s.plan, s.y, wwin, moon.MOON_COMBINE_WEIGHTED, s.out, s.wsk,
-                          stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
-        moon.moon_prefetch_index(ctx, s.plan, s.pidx, stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
+    _, wwin = moon.window_tensors(ctx)
 
     for i in range(max(warmup, len(sets))):  # every input set planned at least once
-        step(i)
+        step_calls(moon, ctx, sets[i % len(sets)], wwin, stream)
     torch.cuda.synchronize()
     for s in sets:
         st = moon.moon_plan_status(s.plan, stream)
@@ -130,27 +139,24 @@ def run_steps(moon, ctx, sets, steps, warmup, stream):
     w0 = time.perf_counter()
     t0.record(stream)
     for i in range(steps):
-        step(i)
+        step_calls(moon, ctx, sets[i % len(sets)], wwin, stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = t0.elapsed_time(t1) / steps
 
     # per-call timing: the same steps again, each call bracketed by events
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
-        step(i, evs[i])
+        step_calls(moon, ctx, sets[i % len(sets)], wwin, stream, evs[i])
     torch.cuda.synchronize()
-    calls = {"plan": 0.0, "dispatch": 0.0, "combine": 0.0, "prefetch_index": 0.0}
-    for ev in evs:
-        calls["plan"] += ev[0].elapsed_time(ev[1])
-        calls["dispatch"] += ev[1].elapsed_time(ev[2])
-        calls["combine"] += ev[2].elapsed_time(ev[3])
-        calls["prefetch_index"] += ev[3].elapsed_time(ev[4])
-    calls = {k: v / steps * 1e3 for k, v in calls.items()}  # microseconds
+    names = ["plan", "dispatch", "combine"]
+    calls = {n: sum(ev[j].elapsed_time(ev[j + 1]) for ev in evs) / steps * 1e3
+             for j, n in enumerate(names)}  # microseconds
 
     # launch durations: the same calls back to back between two events (no
-    # event markers between launches), on the input sets of the timed steps
+    # event markers between launches), on the input sets of the timed steps;
+    # each of dispatch and combine is one kernel launch
     launch = {
         "combine": time_call(lambda i=0: moon.moon_combine(
             ctx, sets[i % len(sets)].plan, sets[i % len(sets)].y, wwin,
@@ -195,17 +201,94 @@ def measure_copy(stream, nbytes=1 << 30, iters=20):
             "GBps": round(2 * nbytes / (t * 1e-6) / 1e9, 1)}
 
 
+_CEIL = None
+
+
+def _ceiling_lib():
+    """The benchmark's reference kernels (libmoon_ceiling.so, built beside libmoon)."""
+    global _CEIL
+    if _CEIL is None:
+        import ctypes
+        import torch  # noqa: F401  (bind to the HIP runtime torch loaded)
+        path = os.path.join(ROOT, "combine_balanced_planning_amd", "libmoon_ceiling.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.moon_ceiling_read.argtypes = [vp, i64, vp, vp]
+        lib.moon_ceiling_fill.argtypes = [vp, i64, vp]
+        lib.moon_ceiling_copy.argtypes = [vp, vp, i64, vp]
+        lib.moon_ceiling_write_rows.argtypes = [vp, vp, i64, i32, i32, vp]
+        lib.moon_ceiling_read_rows.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+        for f in ("read", "fill", "copy", "write_rows", "read_rows"):
+            getattr(lib, "moon_ceiling_" + f).restype = ctypes.c_int
+        _CEIL = lib
+    return _CEIL
+
+
+def measure_ceilings(moon, ctx, s, nb, stream, iters):
+    """What the memory system delivers for the access patterns of the step,
+    each alone, on the step's own buffers and row lists (HIP events, average
+    of back-to-back launches):
+      write_rows  dispatch's stores without its loads (every route's row of
+                  the plan's dst, same grid and slice order as dispatch)
+      read_rows   combine's loads without its stores (the K routed rows of
+                  every token, same grid as combine)
+      fill / read contiguous non-temporal stores / loads over the windows and
+                  the y array
+      copy        contiguous load + store, the token rows into the output
+    The dispatch and combine launch times are put beside them."""
+    import ctypes
+
+    import torch
+    lib = _ceiling_lib()
+    c = ctx.cfg
+    win, _ = moon.window_tensors(ctx)
+    sink = torch.zeros(4, dtype=torch.int32, device=win.device)
+    dst = moon.plan_tensors(s.plan)["dst"]
+    st = ctypes.c_void_p(stream.cuda_stream)
+    row = 2 * c.H
+    ntok = c.R * c.S
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel failed: hip error {rc}")
+
+    legs = {
+        "write_rows": (nb["n_route"] * row, lambda i=0: chk(lib.moon_ceiling_write_rows(
+            win.data_ptr(), dst.data_ptr(), ntok, c.K, c.H, st))),
+        "read_rows": (nb["n_route"] * row, lambda i=0: chk(lib.moon_ceiling_read_rows(
+            s.y.data_ptr(), dst.data_ptr(), ntok, c.K, c.H, sink.data_ptr(), st))),
+        "fill": (win.numel() * 2, lambda i=0: chk(lib.moon_ceiling_fill(
+            win.data_ptr(), win.numel() * 2, st))),
+        "read": (s.y.numel() * 2, lambda i=0: chk(lib.moon_ceiling_read(
+            s.y.data_ptr(), s.y.numel() * 2, sink.data_ptr(), st))),
+        "copy": (2 * s.hidden.numel() * 2, lambda i=0: chk(lib.moon_ceiling_copy(
+            s.hidden.data_ptr(), s.out.data_ptr(), s.hidden.numel() * 2, st))),
+    }
+    out = {}
+    for name, (nbytes, fn) in legs.items():
+        t = time_call(fn, iters, stream)
+        out[name] = {"bytes": int(nbytes), "us": round(t, 2),
+                     "GBps": round(nbytes / (t * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(nbytes / (t * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+    torch.cuda.synchronize()
+    return out
+
+
 def measure_ablations(moon, ctx, s, nb, stream, iters):
-    """The two one-GPU variants of the pages' deduplication on the same input:
-    dispatch writing duplicates from registers (no epilogue re-read) and combine
-    with the duplicate prologue (folds into the window, then gathers primaries)."""
+    """The pages' two-pass structures on the same input: dispatch with the
+    dedup epilogue (the scatter stores primaries only, then the epilogue
+    reads each duplicate group's primary back and stores its duplicates) and
+    combine with the duplicate prologue (folds into the window, then gathers
+    primaries)."""
     c = ctx.cfg
     row = 2 * c.H
     win, wwin = moon.window_tensors(ctx)
-    t_fused = time_call(lambda i=0: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w,
-                                                   flags=moon.MOON_DISPATCH_FUSED_DUPS,
-                                                   stream=stream), iters, stream)
-    t_epi = time_call(lambda i=0: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream),
+    t_epi = time_call(lambda i=0: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w,
+                                                 flags=moon.MOON_DISPATCH_DEDUP_EPILOGUE,
+                                                 stream=stream), iters, stream)
+    t_one = time_call(lambda i=0: moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream),
                       iters, stream)
     flags = moon.MOON_COMBINE_WEIGHTED | moon.MOON_COMBINE_DUP_PROLOGUE
     t_pro = time_call(lambda i=0: moon.moon_combine(ctx, s.plan, s.y, wwin, flags, s.out, s.wsk,
@@ -220,9 +303,10 @@ def measure_ablations(moon, ctx, s, nb, stream, iters):
                  + row * (nb["n_route"] - nb["n_dup"]) + row * c.R * c.S + 4 * nb["n_route"] * 3)
     moon.moon_dispatch(ctx, s.plan, s.hidden, s.w, stream=stream)  # restore the windows
     return {
+        "dispatch_one_pass_us": round(t_one, 2),
         "dispatch_epilogue_us": round(t_epi, 2),
-        "dispatch_fused_dups_us": round(t_fused, 2),
-        "dispatch_fused_dups_GBps": round(nb["dispatch_minimal"] / (t_fused * 1e-6) / 1e9, 1),
+        "dispatch_epilogue_bytes": int(nb["dispatch_epilogue"]),
+        "dispatch_epilogue_GBps": round(nb["dispatch_epilogue"] / (t_epi * 1e-6) / 1e9, 1),
         "combine_plain_us": round(t_plain, 2),
         "combine_dup_prologue_us": round(t_pro, 2),
         "combine_dup_prologue_bytes": int(pro_bytes),
@@ -284,8 +368,8 @@ def measure_weights(moon, ctx, s, stream, iters, hp):
 
 def measure_serving(moon, dev, stream, steps, warmup):
     """The padded serving workload per level: plan (with the tokens_per_expert
-    histogram) -> dispatch -> plain K-sum combine -> prefetch index, timed per
-    call with HIP events on `stream`."""
+    histogram; the prefetch index included) -> dispatch -> plain K-sum
+    combine, timed per call with HIP events on `stream`."""
     import torch
     import synth
     import synth.gpu as sg
@@ -303,7 +387,6 @@ def measure_serving(moon, dev, stream, steps, warmup):
             hidden[r, int(wl["n_tok"][r]):] = 0
         y = sg.y(wl["seed"], R * ctx.NvS, H, dev)
         out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
-        pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
         win, wwin = moon.window_tensors(ctx)
 
         def step(ev=None):
@@ -318,7 +401,6 @@ def measure_serving(moon, dev, stream, steps, warmup):
             moon.moon_combine(ctx, plan, y, None, 0, out, None, stream=stream)
             if ev is not None:
                 ev[3].record(stream)
-            moon.moon_prefetch_index(ctx, plan, pidx, stream=stream)
 
         for _ in range(warmup):
             step()
@@ -538,36 +620,54 @@ def summarize_trace(workload, d, command, bench_line=None):
         f.write("\n".join(lines) + "\n")
 
 
-def cpu_baseline(config, seed, budget_s=12.0):
-    """The oracle, as it stands, on the host: plan + dispatch + combine of the
-    full workload, repeated until about `budget_s` seconds have passed."""
+def cpu_baseline(config, topk, w, seed, budget_s=12.0, sample_tokens=512):
+    """The oracle, as it stands, on one host core.  Its plan is timed once on
+    the full routing; then plan + dispatch + combine run for about `budget_s`
+    seconds on a bounded sample of the same workload: the first
+    `sample_tokens` tokens of every source rank with their routing, their
+    token rows and the routed rows of y drawn from the workload's seeded
+    streams.  Combine runs the oracle's fp32 path alone (its float64
+    reference sum is not computed).  The rate is the sample's dispatch +
+    combine algorithmic bytes over the sample's plan + dispatch + combine
+    time."""
+    import numpy as np
+
     import oracle
     import synth
     c = synth.WORKLOADS[synth.workload_id(config)]
     R, E, K, S, H, B, P = (c[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
-    topk, w = synth.routing(config, seed)
-    hidden = synth.hidden_bf16(seed, R, S, H)
-    nvs = oracle.nvs(R, E, K, S, B, P)
-    y = synth.y_bf16(seed, R * nvs, H)
+    t0 = time.perf_counter()
+    full = oracle.plan(topk, E, B, P)
+    t_full = time.perf_counter() - t0
+    if full.status != oracle.OK:
+        raise RuntimeError(f"oracle plan status {full.status}")
+    Ss = min(S, sample_tokens)
+    topk_s = np.ascontiguousarray(topk[:, :Ss])
+    w_s = np.ascontiguousarray(w[:, :Ss])
+    ids = (np.arange(R)[:, None] * S + np.arange(Ss)[None, :]).reshape(-1)
+    hidden = synth.bf16_rows(synth.stream_key(seed, synth.TAG_HIDDEN), ids, H).reshape(R, Ss, H)
+    pl = oracle.plan(topk_s, E, B, P)
+    rows = np.unique(np.where(pl.dst >= 0, pl.dst, -pl.dst - 1).astype(np.int64))
+    y = np.zeros((R * pl.NvS, H), np.uint16)
+    y[rows] = synth.bf16_rows(synth.stream_key(seed, synth.TAG_Y), rows, H)
+    nb = bytes_from_counts(R, Ss, K, H, *plan_counts(pl.dup_counts, pl.zero_fill_ranges))
+    bytes_dc = nb["dispatch"] + nb["combine"]
     n = 0
     t_plan = t_disp = t_comb = 0.0
     t_start = time.perf_counter()
-    bytes_dc = 0
     while True:
         t0 = time.perf_counter()
-        pl = oracle.plan(topk, E, B, P)
+        pl = oracle.plan(topk_s, E, B, P)
         t1 = time.perf_counter()
-        win, wwin = oracle.dispatch(pl, hidden, w)
+        _, wwin = oracle.dispatch(pl, hidden, w_s)
         t2 = time.perf_counter()
-        oracle.combine(pl, y, wwin, weighted=True)
+        oracle.combine(pl, y, wwin, weighted=True, exact=False)
         t3 = time.perf_counter()
         t_plan += t1 - t0
         t_disp += t2 - t1
         t_comb += t3 - t2
         n += 1
-        if n == 1:
-            nb = bytes_from_counts(R, S, K, H, *plan_counts(pl.dup_counts, pl.zero_fill_ranges))
-            bytes_dc = nb["dispatch"] + nb["combine"]
+        del wwin
         if time.perf_counter() - t_start >= budget_s:
             break
     total = t_plan + t_disp + t_comb
@@ -581,10 +681,114 @@ def cpu_baseline(config, seed, budget_s=12.0):
     avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": round(bytes_dc * n / total / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "host_cpu": model, "host_cores_available": avail,
-            "sample": f"full workload {c['name']} (seed {seed}) x {n}: plan "
-                      f"{t_plan / n * 1e3:.1f} ms, dispatch {t_disp / n * 1e3:.1f} ms, combine "
-                      f"{t_comb / n * 1e3:.1f} ms per step on 1 host core; "
-                      f"{R * S * n / total:.0f} tokens/s"}
+            "tokens_per_s": round(R * Ss * n / total),
+            "plan_full_ms": round(t_full * 1e3, 2),
+            "sample": f"{c['name']} (seed {seed}): oracle plan of the full routing "
+                      f"{t_full * 1e3:.1f} ms; then the first {Ss} of the {S} tokens of every "
+                      f"source rank ({R * Ss} tokens, {bytes_dc / 1e9:.3f} GB of dispatch + "
+                      f"combine bytes) x {n}: plan {t_plan / n * 1e3:.1f} ms, dispatch "
+                      f"{t_disp / n * 1e3:.1f} ms, combine (fp32 path) {t_comb / n * 1e3:.1f} ms "
+                      f"per pass on 1 host core"}
+
+
+def measure_step(moon, config, dev, stream, steps, warmup):
+    """A context and two input sets of `config` (alternated, so a step never
+    finds the previous step's data in the 256 MB last-level cache), the step
+    timing, the step's algorithmic bytes and the roofline figures of its two
+    bulk kernels.  Returns (results, ctx, sets)."""
+    import synth
+    c = synth.WORKLOADS[synth.workload_id(config)]
+    R, E, K, S, H, B, P = (c[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+    log(f"[bench] workload {c['name']}: building inputs")
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    seed = synth.seed_of(config, 0)
+    sets = [Inputs(moon, ctx, config, seed, 0.0, dev),
+            Inputs(moon, ctx, config, seed + 500, 0.0, dev)]
+    log(f"[bench] workload {c['name']}: timing")
+    ms_step, wall, calls, launch = run_steps(moon, ctx, sets, steps, warmup, stream)
+    nbs = [algorithmic_bytes(moon, ctx, s.plan) for s in sets]
+
+    def avg(k):
+        return 0.5 * (nbs[0][k] + nbs[1][k])
+
+    bytes_dc = avg("dispatch") + avg("combine")
+    value = bytes_dc / (ms_step * 1e-3) / 1e9
+    t_dc = (calls["dispatch"] + calls["combine"]) * 1e-6
+    # Roofline figures of the step's two bulk kernels (each call is one
+    # launch): algorithmic bytes per launch over the average launch duration
+    # of back-to-back launches on the timed inputs.
+    kernels = {}
+    for kname, call in (("k_dispatch_scatter", "dispatch"), ("k_combine", "combine")):
+        nbytes = avg(call)
+        ach = nbytes / (launch[call] * 1e-6) / 1e9
+        kernels[kname] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                          "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                          "traffic": measured_traffic(kname, c["name"]), "kernel": kname,
+                          "algorithmic_bytes_per_launch": int(nbytes),
+                          "avg_launch_us": round(launch[call], 2),
+                          "in_step_call_us": round(calls[call], 2)}
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_launch_us"])
+    res = {
+        "workload": c["name"], "R": R, "E": E, "K": K, "S": S, "H": H, "token_padding": P,
+        "B": B, "maxvio": round(sets[0].maxvio, 4), "ms_per_step": round(ms_step, 4),
+        "value": value, "wall_s_timed": round(wall, 4),
+        "tokens_per_s": round(R * S / (ms_step * 1e-3)),
+        "dispatch_combine_GBps": round(bytes_dc / t_dc / 1e9, 1),
+        "tokens_per_s_excl_plan": round(R * S / t_dc),
+        "call_us": {k: round(v, 2) for k, v in calls.items()},
+        "plan_us": round(calls["plan"], 2),
+        "bytes_per_step": {"dispatch": int(avg("dispatch")), "combine": int(avg("combine")),
+                           "dispatch_epilogue": int(avg("dispatch_epilogue")),
+                           "dup_groups": nbs[0]["n_grp"], "dup_rows": nbs[0]["n_dup"],
+                           "pad_rows": nbs[0]["n_pad"]},
+        "slots_used": nbs[0]["slots_used"], "routes_in_slots": nbs[0]["routes_in_slots"],
+        "roofline": kernels[dominant], "kernels": kernels,
+    }
+    return res, ctx, sets, nbs[0]
+
+
+def measure_sweep(moon, ctx, config, base, steps, warmup, stream, dev):
+    """maxvio sweep on the same shapes: the base run, then the skewed levels."""
+    import synth
+    c = synth.WORKLOADS[synth.workload_id(config)]
+    R, S = c["R"], c["S"]
+    sweep = [{"maxvio": base["maxvio"], "ms_per_step": base["ms_per_step"],
+              "GBps": round(base["value"], 1), "tokens_per_s": base["tokens_per_s"],
+              "plan_us": base["plan_us"], "slots_used": base["slots_used"],
+              "routes_in_slots": base["routes_in_slots"]}]
+    sc, levels = SWEEPS[config]
+    for level in levels:
+        target = synth.LEVELS[synth.workload_id(sc)][level]
+        log(f"[bench] maxvio level {target}")
+        s4 = [Inputs(moon, ctx, sc, synth.seed_of(sc, level), synth.alpha_for(sc, level), dev),
+              Inputs(moon, ctx, sc, synth.seed_of(sc, level) + 500, synth.alpha_for(sc, level),
+                     dev)]
+        ms4, _, calls4, _ = run_steps(moon, ctx, s4, steps, warmup, stream)
+        b4 = [algorithmic_bytes(moon, ctx, s.plan) for s in s4]
+        by4 = 0.5 * sum(b["dispatch"] + b["combine"] for b in b4)
+        sweep.append({"maxvio": round(s4[0].maxvio, 4), "target": target,
+                      "ms_per_step": round(ms4, 4), "GBps": round(by4 / (ms4 * 1e-3) / 1e9, 1),
+                      "tokens_per_s": round(R * S / (ms4 * 1e-3)),
+                      "plan_us": round(calls4["plan"], 2),
+                      "dispatch_us": round(calls4["dispatch"], 2),
+                      "combine_us": round(calls4["combine"], 2),
+                      "slots_used": b4[0]["slots_used"],
+                      "routes_in_slots": b4[0]["routes_in_slots"]})
+        for s in s4:
+            moon.moon_plan_destroy(s.plan)
+        del s4
+    times = [p["ms_per_step"] for p in sweep]
+    return sweep, round(max(times) / min(times), 4)
+
+
+def release(moon, ctx, sets):
+    import torch
+    for s in sets:
+        moon.moon_plan_destroy(s.plan)
+    moon.moon_ctx_destroy(ctx)
+    sets.clear()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def main():
@@ -592,12 +796,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="r8-e64-k6", choices=["r8-e64-k6", "dsv3", "r16-e384-k8"])
+    ap.add_argument("--workload", default=HEADLINE, choices=["r16-e384-k8", "dsv3", "r8-e64-k6"])
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary r8-e64-k6 section")
     ap.add_argument("--step-only", action="store_true",
-                    help="time the step only: no ablations, weights, serving workload, maxvio "
-                         "sweep or CPU baseline (the counter runs use this)")
+                    help="time the step only: no ceilings, ablations, sweep, secondary section "
+                         "or CPU baseline (the counter runs use this)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="run only a plain 1 GiB elementwise copy (scales HBM counters)")
@@ -639,135 +845,91 @@ def main():
         return
 
     import combine_balanced_planning_amd as moon
-    import synth
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     config = args.workload
-    c = synth.WORKLOADS[synth.workload_id(config)]
-    R, E, K, S, H, B, P = (c[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
-    log(f"[bench] workload {c['name']}: building inputs")
-    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
-    seed = synth.seed_of(config, 0)
-    # two input sets, alternated, so a step never finds the previous step's
-    # data in the 256 MB last-level cache
-    sets = [Inputs(moon, ctx, config, seed, 0.0, dev),
-            Inputs(moon, ctx, config, seed + 500, 0.0, dev)]
-    torch.cuda.synchronize()
-    log("[bench] timing")
-    ms_step, wall, calls, launch = run_steps(moon, ctx, sets, args.steps, args.warmup, stream)
-    nb = algorithmic_bytes(moon, ctx, sets[0].plan)
-    nb1 = algorithmic_bytes(moon, ctx, sets[1].plan)
-    bytes_dc = 0.5 * (nb["dispatch"] + nb["combine"] + nb1["dispatch"] + nb1["combine"])
-    value = bytes_dc / (ms_step * 1e-3) / 1e9
-    t_dc = (calls["dispatch"] + calls["combine"]) * 1e-6
-    dc_gbps = bytes_dc / t_dc / 1e9
+    full = not args.step_only
+    head, ctx, sets, nb0 = measure_step(moon, config, dev, stream, args.steps, args.warmup)
 
-    # Roofline of the dominant kernel: k_combine, the largest single launch of
-    # the step (one launch per combine call); its duration is the average of
-    # back-to-back launches on the timed inputs.  Dispatch is two launches
-    # (scatter + epilogue); its call-level figure is reported beside it.
-    comb_bytes = 0.5 * (nb["combine"] + nb1["combine"])
-    disp_bytes = 0.5 * (nb["dispatch"] + nb1["dispatch"])
-    achieved = comb_bytes / (launch["combine"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                "traffic": measured_traffic("k_combine", c["name"]),
-                "kernel": "k_combine", "algorithmic_bytes_per_launch": int(comb_bytes),
-                "avg_launch_us": round(launch["combine"], 2),
-                "in_step_call_us": round(calls["combine"], 2)}
-    disp_gbps = disp_bytes / (launch["dispatch"] * 1e-6) / 1e9
-    t_sc = measured_traffic("k_dispatch_scatter", c["name"])
-    t_ex = measured_traffic("k_dispatch_expand", c["name"])
-    dispatch_roofline = {"kernels": "k_dispatch_scatter + k_dispatch_expand",
-                         "achieved": round(disp_gbps, 1), "unit": "GB/s",
-                         "frac": round(disp_gbps / PEAK_HBM_GBPS, 4),
-                         "traffic": t_sc + t_ex if t_sc is not None and t_ex is not None else None,
-                         "algorithmic_bytes_per_call": int(disp_bytes),
-                         "avg_call_us": round(launch["dispatch"], 2),
-                         "in_step_call_us": round(calls["dispatch"], 2)}
-
-    ablations = weights = serving = copy = None
-    if not args.step_only:
+    ceilings = ablations = weights = serving = copy = cpu = secondary = None
+    sweep, flat = [], None
+    iters = max(10, args.steps // 5)
+    if full:
+        log("[bench] memory-system ceilings")
+        ceilings = measure_ceilings(moon, ctx, sets[0], nb0, stream, iters)
         copy = measure_copy(stream)
-        roofline["frac_of_measured_copy"] = round(achieved / copy["GBps"], 4)
-        dispatch_roofline["frac_of_measured_copy"] = round(disp_gbps / copy["GBps"], 4)
-        ablations = measure_ablations(moon, ctx, sets[0], nb, stream, max(10, args.steps // 2))
+        k = head["kernels"]
+        k["k_dispatch_scatter"]["write_rows_us_over_launch_us"] = round(
+            ceilings["write_rows"]["us"] / k["k_dispatch_scatter"]["avg_launch_us"], 4)
+        k["k_combine"]["read_rows_us_over_launch_us"] = round(
+            ceilings["read_rows"]["us"] / k["k_combine"]["avg_launch_us"], 4)
+        for kk in k.values():
+            kk["frac_of_measured_copy"] = round(kk["achieved"] / ceilings["copy"]["GBps"], 4)
+        log("[bench] ablations")
+        ablations = measure_ablations(moon, ctx, sets[0], nb0, stream, iters)
         if config in FFN_WIDTH:
             log("[bench] weight prefetch and gradient reduction")
             weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
                                       FFN_WIDTH[config])
-        if config == "r8-e64-k6":
+        if not args.no_sweep and config in SWEEPS:
+            sweep, flat = measure_sweep(moon, ctx, config, head, max(10, args.steps // 2),
+                                        args.warmup, stream, dev)
+        topk_h, w_h, seed0 = sets[0].topk_h, sets[0].w_h, sets[0].seed
+        release(moon, ctx, sets)
+        if not args.no_secondary and config != SECONDARY:
+            sec, sctx, ssets, _ = measure_step(moon, SECONDARY, dev, stream, args.steps,
+                                               args.warmup)
+            secondary = dict(sec, cache_affected=True)
+            secondary["value"] = round(secondary["value"], 1)
+            secondary["pct_of_hbm_peak"] = round(100 * sec["value"] / PEAK_HBM_GBPS, 2)
+            log("[bench] weight prefetch and gradient reduction (secondary)")
+            secondary["weights"] = measure_weights(moon, sctx, ssets[0], stream,
+                                                   max(5, args.steps // 10),
+                                                   FFN_WIDTH[SECONDARY])
+            if not args.no_sweep:
+                secondary["maxvio_sweep"], secondary["sweep_max_over_min_time"] = measure_sweep(
+                    moon, sctx, SECONDARY, sec, max(10, args.steps // 2), args.warmup, stream,
+                    dev)
+            release(moon, sctx, ssets)
+        if config == SECONDARY or not args.no_secondary:
             log("[bench] padded serving workload")
             serving = measure_serving(moon, dev, stream, max(10, args.steps // 5), 3)
-
-    sweep = []
-    if not args.no_sweep and not args.step_only and config in SWEEPS:
-        # maxvio sweep on the same shapes: level "0" is this workload's routing,
-        # then the skewed levels
-        sweep.append({"maxvio": round(sets[0].maxvio, 4), "ms_per_step": round(ms_step, 4),
-                      "GBps": round(value, 1), "tokens_per_s": round(R * S / (ms_step * 1e-3))})
-        sc, levels = SWEEPS[config]
-        for level in levels:
-            target = synth.LEVELS[synth.workload_id(sc)][level]
-            log(f"[bench] maxvio level {target}")
-            s4 = [Inputs(moon, ctx, sc, synth.seed_of(sc, level), synth.alpha_for(sc, level), dev),
-                  Inputs(moon, ctx, sc, synth.seed_of(sc, level) + 500,
-                         synth.alpha_for(sc, level), dev)]
-            ms4, _, calls4, _ = run_steps(moon, ctx, s4, max(10, args.steps // 2), args.warmup,
-                                          stream)
-            b4 = [algorithmic_bytes(moon, ctx, s.plan) for s in s4]
-            by4 = 0.5 * sum(b["dispatch"] + b["combine"] for b in b4)
-            sweep.append({"maxvio": round(s4[0].maxvio, 4), "target": target,
-                          "ms_per_step": round(ms4, 4), "GBps": round(by4 / (ms4 * 1e-3) / 1e9, 1),
-                          "tokens_per_s": round(R * S / (ms4 * 1e-3)),
-                          "plan_us": round(calls4["plan"], 2),
-                          "slots_used": b4[0]["slots_used"],
-                          "routes_in_slots": b4[0]["routes_in_slots"]})
-            for s in s4:
-                moon.moon_plan_destroy(s.plan)
-            del s4
-        times = [p["ms_per_step"] for p in sweep]
-        flat = max(times) / min(times)
+        if not args.no_cpu_baseline:
+            log("[bench] cpu baseline (oracle)")
+            cpu = cpu_baseline(config, topk_h, w_h, seed0, args.cpu_budget)
     else:
-        flat = None
-
-    cpu = None
-    if not args.no_cpu_baseline and not args.step_only:
-        log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(config, seed, args.cpu_budget)
+        release(moon, ctx, sets)
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": round(head["value"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded routing, bf16 N(0,1) activations)",
-        "config": {"workload": c["name"], "R": R, "E": E, "K": K, "S": S, "H": H,
-                   "token_padding": P, "B": B, "maxvio": round(sets[0].maxvio, 4),
-                   "global_batch": R * S, "parallelism": "ep emulated as R windows on 1 GPU"},
-        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
-        "tokens_per_s": round(R * S / (ms_step * 1e-3)),
-        "dispatch_combine_GBps": round(dc_gbps, 1),
-        "tokens_per_s_excl_plan": round(R * S / t_dc),
-        "call_us": {k: round(v, 2) for k, v in calls.items()},
-        "plan_us": round(calls["plan"], 2),
-        "bytes_per_step": {"dispatch": int(disp_bytes), "combine": int(comb_bytes),
-                           "dispatch_minimal": int(0.5 * (nb["dispatch_minimal"] +
-                                                          nb1["dispatch_minimal"])),
-                           "dup_rows": nb["n_dup"], "pad_rows": nb["n_pad"]},
-        "maxvio_sweep": sweep, "sweep_max_over_min_time": round(flat, 4) if flat else None,
-        "wall_s_timed": round(wall, 4),
-        "roofline": roofline,
-        "dispatch_roofline": dispatch_roofline,
-        "ablations": ablations,
+        "config": {"workload": head["workload"], "R": head["R"], "E": head["E"],
+                   "K": head["K"], "S": head["S"], "H": head["H"],
+                   "token_padding": head["token_padding"], "B": head["B"],
+                   "maxvio": head["maxvio"], "global_batch": head["R"] * head["S"],
+                   "parallelism": "ep emulated as R windows on 1 GPU"},
+        "pct_of_hbm_peak": round(100 * head["value"] / PEAK_HBM_GBPS, 2),
+        "tokens_per_s": head["tokens_per_s"],
+        "dispatch_combine_GBps": head["dispatch_combine_GBps"],
+        "tokens_per_s_excl_plan": head["tokens_per_s_excl_plan"],
+        "call_us": head["call_us"], "plan_us": head["plan_us"],
+        "bytes_per_step": head["bytes_per_step"],
+        "slots_used": head["slots_used"], "routes_in_slots": head["routes_in_slots"],
+        "maxvio_sweep": sweep, "sweep_max_over_min_time": flat,
+        "wall_s_timed": head["wall_s_timed"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "ceilings": ceilings,
         "plain_copy": copy,
+        "ablations": ablations,
         "weights": weights,
+        "secondary": secondary,
         "serving": serving,
         "cpu_baseline": cpu,
     }
-    for s in sets:
-        moon.moon_plan_destroy(s.plan)
-    moon.moon_ctx_destroy(ctx)
     print(json.dumps(line), flush=True)
 
 

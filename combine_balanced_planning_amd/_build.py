@@ -20,16 +20,28 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False):
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    tmp = SO + ".tmp"
+# Reference kernels of the benchmark (memory-system ceilings for the access
+# patterns of dispatch and combine); a library of their own, not part of
+# libmoon.
+CEILING_SO = os.path.join(HERE, "libmoon_ceiling.so")
+CEILING_SOURCES = ["moon_ceiling.hip"]
+
+
+def _hipcc_shared(sources, so, verbose):
+    srcs = [os.path.join(HERE, "csrc", s) for s in sources]
+    tmp = so + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), *srcs,
            "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, SO)
-    return SO
+    os.replace(tmp, so)
+    return so
+
+
+def build(verbose=False):
+    _hipcc_shared(CEILING_SOURCES, CEILING_SO, verbose)
+    return _hipcc_shared(SOURCES, SO, verbose)
 
 
 # A C11 program that uses libmoon.so through include/moon.h only (hipMalloc'd

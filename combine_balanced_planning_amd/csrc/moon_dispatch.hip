@@ -10,8 +10,8 @@
 // of the bytes are writes to scattered rows.
 //
 //   k_dispatch_scatter<FUSED=true>   (the default) persistent grid; a work
-//                       item is one wave on a 2 KB slice (128 vectors) of one
-//                       token's row, read once with plain loads and stored
+//                       item is one wave on a 2 KB slice (128 vectors; 1 KB
+//                       for rows of at most 4 KB) of one token's row, read once with plain loads and stored
 //                       with non-temporal stores to the rows of all K routes
 //                       (primaries and duplicates alike: a duplicate row gets
 //                       the same bits from registers, so no second pass reads
@@ -45,8 +45,14 @@ constexpr int kThreads = kWavesPerBlock * kWave;
 // / 3875 / 3886 / 3874, where 4 leaves the last of four slices of a 14 KB row
 // half empty.
 constexpr int kSliceVec = 7;
-// The same for the fused scatter, which stores each slice K times.
+// The same for the one-pass scatter, which stores each slice K times: 2 KB
+// slices for wide rows, 1 KB slices for rows of at most 4 KB.  Measured
+// dispatch µs for widths 1 / 2 / 4 / 7 (32768 workgroups; 8192 were 0.6 %
+// slower at the R=16 shape): R=16 shape (14 KB rows) 3533 / 3403 / 3463 /
+// 3568; r8-e64-k6 (4 KB rows) 77.9 / 80.7 / 84.0 / 85.0.
 constexpr int kFusedSliceVec = 2;
+constexpr int kFusedSliceVecNarrow = 1;
+constexpr int kNarrowRowVec = 256;  // 4 KB rows
 // Padding rows per zero-fill item (a sweep of 1, 2, 4, 8, 16: 2 is 5 % faster
 // than 8 at serving decode, where padding dominates, and equal elsewhere).
 constexpr int kZeroRows = 2;
@@ -252,9 +258,14 @@ hipError_t launch_dispatch(const Dims& d, const PlanArrays& pa, const uint16_t* 
   const auto* hv = reinterpret_cast<const u32x4*>(hidden);
   auto* wv = reinterpret_cast<u32x4*>(win);
   if (!epilogue || d.K == 1) {
-    hipLaunchKernelGGL((k_dispatch_scatter<kFusedSliceVec, true>),
-                       dim3(scatter_blocks<kFusedSliceVec>(d)), dim3(kThreads), 0, s, d, pa, hv, w,
-                       wv, wwin, 0);
+    if (d.H / 8 <= kNarrowRowVec)
+      hipLaunchKernelGGL((k_dispatch_scatter<kFusedSliceVecNarrow, true>),
+                         dim3(scatter_blocks<kFusedSliceVecNarrow>(d)), dim3(kThreads), 0, s, d,
+                         pa, hv, w, wv, wwin, 0);
+    else
+      hipLaunchKernelGGL((k_dispatch_scatter<kFusedSliceVec, true>),
+                         dim3(scatter_blocks<kFusedSliceVec>(d)), dim3(kThreads), 0, s, d, pa, hv,
+                         w, wv, wwin, 0);
     return hipGetLastError();
   }
   // The epilogue re-reads one primary row per duplicate group (about 1.3

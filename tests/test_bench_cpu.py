@@ -137,16 +137,20 @@ def test_algorithmic_bytes_by_hand():
              + routes * 12       # dst read, weight read, weight written
              + 5 * 4             # padding weights zeroed
              + 1 * 12 + 2 * 4)   # the duplicate record and its two row offsets
-    assert nb["dispatch_minimal"] == d_min
-    assert nb["dispatch"] == d_min + 1 * row  # the epilogue reads the group's primary once
+    assert nb["dispatch"] == d_min  # one pass: duplicates stored from the token's row
+    assert nb["dispatch_epilogue"] == d_min + 1 * row  # the epilogue reads the primary once
     assert nb["combine"] == routes * row + tokens * row + routes * 12
     assert bench.plan_counts(np.array([[1, 1], [0, 0]]),
                              np.array([[[3, 5], [7, 7]], [[0, 3], [9, 9]]])) == (1, 1, 5)
 
 
 def test_cpu_baseline_record():
-    """The oracle timed on the host: one pass of the full workload is enough
-    to fill the record the bench line carries."""
-    rec = bench.cpu_baseline(2, 2000, budget_s=0.0)
+    """The oracle timed on the host: its plan of the full routing, then one
+    pass over the token sample is enough to fill the record the bench line
+    carries."""
+    import synth
+    topk, w = synth.routing("r8-e64-k6", 2000)
+    rec = bench.cpu_baseline("r8-e64-k6", topk, w, 2000, budget_s=0.0, sample_tokens=64)
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "GB/s"
-    assert rec["value"] > 0 and " x 1: plan " in rec["sample"]
+    assert rec["value"] > 0 and rec["tokens_per_s"] > 0 and rec["plan_full_ms"] > 0
+    assert "the first 64 of the 2048 tokens" in rec["sample"] and ") x 1: plan " in rec["sample"]
