@@ -86,10 +86,11 @@ _lib.moon_reduce_grad.argtypes = [_vp, _vp, _P(moon_grad_tensor), _i32, _vp]
 _lib.moon_status_str.argtypes = [_i32]
 _lib.moon_status_str.restype = ctypes.c_char_p
 _lib.moon_debug_tile_counts.argtypes = [_vp, _vp, _P(_i32), _P(_i32), _vp]
+_lib.moon_plan_noalloc.argtypes = [_P(moon_config), _vp, _vp, _P(moon_plan_arrays), _vp]
 for _f in ("moon_ctx_create", "moon_ctx_layout", "moon_plan_create", "moon_plan_clone",
            "moon_plan_view", "moon_plan_status", "moon_plan", "moon_dispatch", "moon_combine",
            "moon_prefetch_index", "moon_prefetch_weight", "moon_reduce_grad",
-           "moon_debug_tile_counts"):
+           "moon_debug_tile_counts", "moon_plan_noalloc"):
     getattr(_lib, _f).restype = _i32
 
 
@@ -308,6 +309,39 @@ def device_view(ptr, shape, dtype, device=None):
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
     t = torch.as_tensor(_CudaArray(ptr, shape, typestr), device=dev)
     return t.view(torch.bfloat16) if dtype == torch.bfloat16 else t
+
+
+def plan_array_shapes(R, E, K, S, B, token_padding):
+    """Shapes of the plan arrays (all int32) for moon_plan_noalloc, with the
+    capacity NvS = round_up(S*K + (E/R + B)*(P - 1), P) documented at
+    moon_ctx_create and B <= 0 meaning E/R.  Returns (shapes, NvS, B)."""
+    B = B if B > 0 else E // R
+    P = token_padding
+    NvS = (S * K + (E // R + B) * (P - 1) + P - 1) // P * P
+    EB = E + B
+    return ({"dst": (R, S * K), "experts_to_copy": (R, B), "zero_fill_ranges": (R, EB, 2),
+             "remote_stats": (R, 2), "dup_groups": (R, NvS, 3), "dup_loffs": (R, NvS),
+             "dup_counts": (R, 2), "cu_seqlens": (R, EB), "status": (1,),
+             "prefetch_index": (R, B, 2)}, NvS, B)
+
+
+def moon_plan_noalloc(R, E, K, S, H, B, token_padding, topk, tokens_per_expert, arrays,
+                      stream=None):
+    """Planning without a context into caller-owned arrays (a dict of int32
+    device tensors with the shapes of plan_array_shapes); allocates nothing."""
+    shapes, NvS, Bx = plan_array_shapes(R, E, K, S, B, token_padding)
+    cfg = moon_config(R, E, K, S, H, B, token_padding, 0)
+    pa = moon_plan_arrays()
+    for k, shp in shapes.items():
+        n = 1
+        for x in shp:
+            n *= x
+        setattr(pa, k, _ptr(arrays[k], torch.int32, n, k))
+    pa.N, pa.R, pa.E, pa.B, pa.NvS, pa.K = S * K, R, E, Bx, NvS, K
+    _check(_lib.moon_plan_noalloc(ctypes.byref(cfg), _ptr(topk, torch.int32, R * S * K, "topk"),
+                                  _ptr(tokens_per_expert, torch.int32, R * E, "tokens_per_expert",
+                                       optional=True), ctypes.byref(pa), _stream(stream)),
+           "moon_plan_noalloc")
 
 
 def plan_tensors(plan):

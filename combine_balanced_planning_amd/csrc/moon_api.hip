@@ -9,8 +9,21 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "moon_internal.h"
+
+// The largest planner scratch moon_plan_noalloc serves (the count matrix,
+// the exchange words and the call tag): 512 KB holds every shape up to
+// E = 384 with 256 planner tiles; the largest ones (E = 512 with more than
+// about 220 tiles) are refused.
+constexpr size_t kNoAllocScratchBytes = 512u << 10;
+
+// Planner scratch of moon_plan_noalloc: one block on every GPU the library
+// runs on, held until the process ends.  Host code reaches it only through
+// the device address that hipGetSymbolAddress gives for the current device
+// (noalloc_scratch); the array's name is not a device address on the host.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -124,6 +137,14 @@ size_t carve(size_t& off, size_t bytes) {
   return at;
 }
 
+moon::Scratch scratch_at(char* base, const moon::ScratchLayout& sl) {
+  moon::Scratch sc;
+  sc.tile_cnt = reinterpret_cast<int32_t*>(base + sl.cnt);
+  sc.tile_agg = reinterpret_cast<uint64_t*>(base + sl.agg);
+  sc.epoch = reinterpret_cast<uint32_t*>(base + sl.epoch);
+  return sc;
+}
+
 // Offsets of the plan arrays inside one allocation.
 struct PlanOffsets {
   size_t dst, etc, zfr, rstats, dup_groups, dup_loffs, dup_counts, cu, status, pidx, total;
@@ -181,7 +202,38 @@ moon_status new_plan(moon_ctx* ctx, moon_comm_plan** out) {
   return MOON_OK;
 }
 
+// Device address of this GPU's planner scratch block, taken once per device
+// with that device current; nullptr if the runtime refuses.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+void* noalloc_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
+
+namespace moon {
+
+ScratchLayout scratch_layout(const Dims& d) {
+  ScratchLayout sl;
+  size_t off = 0;
+  sl.cnt = carve(off, (size_t)(d.E + 1) * d.ntiles_pad * sizeof(int32_t));
+  sl.agg = carve(off, (size_t)d.ntiles * d.R * 8);
+  sl.epoch = carve(off, sizeof(uint32_t));
+  sl.total = (off + 255) & ~(size_t)255;
+  return sl;
+}
+
+}  // namespace moon
 
 extern "C" {
 
@@ -204,11 +256,9 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
     return MOON_ERR_HIP;
   }
   const size_t rows = (size_t)d.R * d.NvS;
-  size_t off = 0;
+  const moon::ScratchLayout sl = moon::scratch_layout(d);
+  size_t off = sl.total;
   const size_t i4 = sizeof(int32_t);
-  const size_t o_cnt = carve(off, (size_t)(d.E + 1) * d.ntiles_pad * i4);
-  const size_t o_agg = carve(off, (size_t)d.ntiles * d.R * 8);
-  const size_t o_epoch = carve(off, i4);
   const size_t o_used = carve(off, (size_t)d.R * d.B * i4);
   const size_t o_acte = carve(off, (size_t)d.E * i4);
   const size_t o_actm = carve(off, (size_t)d.E * d.R * i4);
@@ -226,9 +276,7 @@ moon_status moon_ctx_create(const moon_config* cfg, moon_ctx** out) {
     return MOON_ERR_HIP;
   }
   char* b = static_cast<char*>(c->scratch_mem);
-  c->sc.tile_cnt = reinterpret_cast<int32_t*>(b + o_cnt);
-  c->sc.tile_agg = reinterpret_cast<uint64_t*>(b + o_agg);
-  c->sc.epoch = reinterpret_cast<uint32_t*>(b + o_epoch);
+  c->sc = scratch_at(b, sl);
   c->si.used = reinterpret_cast<int32_t*>(b + o_used);
   c->si.act_e = reinterpret_cast<int32_t*>(b + o_acte);
   c->si.act_match = reinterpret_cast<int32_t*>(b + o_actm);
@@ -369,6 +417,45 @@ moon_status moon_plan(moon_ctx* ctx, const int32_t* topk_rsk, const int32_t* tok
   DeviceGuard g(ctx->device);
   if (moon::launch_plan(ctx->d, ctx->sc, plan->a, topk_rsk, tokens_per_expert_re, stream) !=
       hipSuccess)
+    return MOON_ERR_HIP;
+  return MOON_OK;
+}
+
+moon_status moon_plan_noalloc(const moon_config* cfg, const int32_t* topk_rsk,
+                              const int32_t* tokens_per_expert_re, const moon_plan_arrays* plan,
+                              hipStream_t stream) {
+  if (plan == nullptr || topk_rsk == nullptr) return MOON_ERR_INVALID_ARG;
+  Dims d;
+  moon_status st = make_dims(cfg, &d);
+  if (st != MOON_OK) return st;
+  const moon_plan_arrays& p = *plan;
+  if (p.N != d.S * d.K || p.R != d.R || p.E != d.E || p.B != d.B || p.NvS != d.NvS || p.K != d.K)
+    return MOON_ERR_INVALID_ARG;
+  const int32_t* arrays[] = {p.dst, p.experts_to_copy, p.zero_fill_ranges, p.remote_stats,
+                             p.dup_groups, p.dup_loffs, p.dup_counts, p.cu_seqlens, p.status,
+                             p.prefetch_index, topk_rsk};
+  for (const int32_t* a : arrays)
+    if (a == nullptr || !aligned(a, 4)) return MOON_ERR_INVALID_ARG;
+  if (!aligned(tokens_per_expert_re, 4)) return MOON_ERR_INVALID_ARG;
+  const moon::ScratchLayout sl = moon::scratch_layout(d);
+  if (sl.total > kNoAllocScratchBytes) return MOON_ERR_UNSUPPORTED;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOON_ERR_HIP;
+  void* base = noalloc_scratch(dev);
+  if (base == nullptr) return MOON_ERR_HIP;
+  moon::PlanArrays pa;
+  pa.dst = p.dst;
+  pa.etc = p.experts_to_copy;
+  pa.zfr = p.zero_fill_ranges;
+  pa.rstats = p.remote_stats;
+  pa.dup_groups = p.dup_groups;
+  pa.dup_loffs = p.dup_loffs;
+  pa.dup_counts = p.dup_counts;
+  pa.cu = p.cu_seqlens;
+  pa.status = p.status;
+  pa.pidx = p.prefetch_index;
+  if (moon::launch_plan(d, scratch_at(static_cast<char*>(base), sl), pa, topk_rsk,
+                        tokens_per_expert_re, stream) != hipSuccess)
     return MOON_ERR_HIP;
   return MOON_OK;
 }

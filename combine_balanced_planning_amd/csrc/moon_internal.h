@@ -35,13 +35,21 @@ struct Dims {
   int32_t tbits;           // bits needed for a token index inside a chunk
 };
 
-// Planner scratch owned by a context (one allocation).
+// Planner scratch: owned by a context (one allocation), or the library's
+// static device array for moon_plan_noalloc.
 struct Scratch {
   int32_t* tile_cnt;     // [E+1][ntiles_pad] routes of expert e in tile t; row E holds 1
-                         // for a tile with an id outside [0,E); padding columns stay 0
+                         // for a tile with an id outside [0,E); padding columns are 0
   uint64_t* tile_agg;    // [ntiles][R] packed (tag, duplicate groups, duplicate rows) per rank
-  uint32_t* epoch;       // [1] tag of the latest planning call
+  uint32_t* epoch;       // [1] tag of the latest planning call (low 16 bits never 0)
 };
+
+// Byte offsets of the planner scratch arrays inside one block, 256-byte
+// aligned; `total` is the block size.
+struct ScratchLayout {
+  size_t cnt, agg, epoch, total;
+};
+ScratchLayout scratch_layout(const Dims& d);
 
 // Slot index of a plan, rebuilt by every weight prefetch and gradient
 // reduction call (context scratch).

@@ -137,10 +137,21 @@ __global__ void __launch_bounds__(kPlanThreads)
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kPlanThreads) sc.tile_cnt[e * d.ntiles_pad + t] = cnt[e];
   if (threadIdx.x == 0) sc.tile_cnt[E * d.ntiles_pad + t] = sBad;
+  // The scratch may hold an earlier call's data of another shape: the last
+  // tile zeroes the padding columns of the count matrix (read in whole
+  // 16-byte groups), and every tile resets its words of the duplicate-count
+  // exchange to tag 0, which no call uses, so no word left by an earlier call
+  // can pass for one of this call's.
+  const int npad = d.ntiles_pad - d.ntiles;
+  if (t == d.ntiles - 1)
+    for (int x = threadIdx.x; x < (E + 1) * npad; x += kPlanThreads)
+      sc.tile_cnt[(x / npad) * d.ntiles_pad + d.ntiles + x % npad] = 0;
+  for (int u = threadIdx.x; u < d.R; u += kPlanThreads) sc.tile_agg[t * d.R + u] = 0;
   if (t == 0 && threadIdx.x == 0) {
     pa.status[0] = 0;  // k_plan_place ORs in what it finds
-    const uint32_t next = sc.epoch[0] + 1u;  // tag of this call's words in k_plan_place
-    sc.epoch[0] = next == 0u ? 1u : next;
+    uint32_t next = sc.epoch[0] + 1u;  // tag of this call's words in k_plan_place
+    if ((next & 0xFFFFu) == 0u) next += 1u;  // tag 0 marks a reset word
+    sc.epoch[0] = next;
   }
 }
 

@@ -167,6 +167,26 @@ moon_status moon_plan_status(const moon_comm_plan* plan, hipStream_t stream);
 moon_status moon_plan(moon_ctx* ctx, const int32_t* topk_rsk, const int32_t* tokens_per_expert_re,
                       moon_comm_plan* plan, hipStream_t stream);
 
+/* Planning that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The same planning as moon_plan, without a context: cfg
+ * gives the shapes (validated as by moon_ctx_create, nothing allocated);
+ * `plan` holds caller-owned device arrays for every field of
+ * moon_plan_arrays, sized for cfg, with N, R, E, B, NvS and K set to the
+ * values cfg implies (NvS as at moon_ctx_create, B the effective slot count)
+ * -- any other value is MOON_ERR_INVALID_ARG.  The planner's scratch is a
+ * fixed 512 KB block in the library's device memory, one per GPU (its address
+ * is taken once per device, on the first call with that device current); a
+ * shape whose scratch exceeds it is refused with MOON_ERR_UNSUPPORTED.  Every
+ * call on one GPU shares that block: calls that overlap on one GPU (two
+ * streams, two host threads) race and their plans are undefined.  The
+ * block keeps the last call's contents; each call resets what it reads.
+ * Results (including the device status word, read by the caller from
+ * plan->status: 0 = OK, else error bits) are bit-identical to moon_plan's. */
+moon_status moon_plan_noalloc(const moon_config* cfg, const int32_t* topk_rsk,
+                              const int32_t* tokens_per_expert_re, const moon_plan_arrays* plan,
+                              hipStream_t stream);
+
 /* Dispatch with a plan (Guide, Buffer.dispatch): hidden_rsh [R,S,H] bf16
  * token rows are copied once per destination rank to their primary rows,
  * weights_rsk [R,S,K] fp32 (optional) go to every route's row, padding rows
