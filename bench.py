@@ -620,6 +620,64 @@ def summarize_trace(workload, d, command, bench_line=None):
         f.write("\n".join(lines) + "\n")
 
 
+# Memory-queue counters of the L2 (TCC) to memory interface, two passes
+# (at most four TCC counters a pass), each with the GPU's busy cycles.
+STALL_PASSES = [["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_sum",
+                 "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "GRBM_GUI_ACTIVE"],
+                ["TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum", "TCC_TAG_STALL_sum",
+                 "TCC_EA0_WRREQ_LEVEL_sum", "TCC_EA0_RDREQ_LEVEL_sum", "GRBM_GUI_ACTIVE"]]
+STALL_KERNELS = ["k_dispatch_scatter", "k_combine", "k_write_rows", "k_read_rows", "k_fill",
+                 "k_read", "k_copy"]
+
+
+def read_counter_table(d):
+    """{kernel: {counter: mean value per dispatch}} from a rocprofv3 --pmc csv folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                k = short_kernel_name(row["Kernel_Name"]).split("<", 1)[0]
+                per = acc.setdefault(k, {}).setdefault(row["Counter_Name"], {})
+                per[row.get("Dispatch_Id", len(per))] = float(row["Counter_Value"])
+    return {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def summarize_stalls(workload, dirs, commands):
+    """profiles/stalls_<workload>.md: per kernel of the step and of the ceiling
+    legs, the L2-to-memory requests and queue occupancy per busy cycle and the
+    cycles requests waited for memory-controller credit."""
+    a, b = (read_counter_table(d) for d in dirs)
+    lines = [f"# Memory-queue counters — workload {workload}", "",
+             "Commands (repo root, one MI355X):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", "Per kernel, means over its launches; counters are sums over the L2 "
+              "channels, divided by the GPU's busy cycles (GRBM_GUI_ACTIVE).  Requests to "
+              "memory are 64 B (writes) and 128 B (reads) here.", "",
+              "| kernel | busy cycles | write req / cycle | read req / cycle | writes in flight "
+              "| reads in flight | write-credit stall / cycle | read-credit stall / cycle "
+              "| tag stall / cycle |", "|---|---|---|---|---|---|---|---|---|"]
+    for k in STALL_KERNELS:
+        if k not in a or k not in b:
+            continue
+        ca, cb = a[k], b[k]
+        cyc = ca["GRBM_GUI_ACTIVE"]
+        cyc_b = cb["GRBM_GUI_ACTIVE"]
+        lines.append(
+            f"| {k} | {cyc:.4g} | {ca['TCC_EA0_WRREQ_sum'] / cyc:.3f} | "
+            f"{ca['TCC_EA0_RDREQ_sum'] / cyc:.3f} | {cb['TCC_EA0_WRREQ_LEVEL_sum'] / cyc_b:.0f} | "
+            f"{cb['TCC_EA0_RDREQ_LEVEL_sum'] / cyc_b:.0f} | "
+            f"{cb['TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum'] / cyc_b:.3f} | "
+            f"{ca['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / cyc:.3f} | "
+            f"{cb['TCC_TAG_STALL_sum'] / cyc_b:.3f} |")
+    with open(os.path.join(PROFILES, f"stalls_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def cpu_baseline(config, topk, w, seed, budget_s=12.0, sample_tokens=512):
     """The oracle, as it stands, on one host core.  Its plan is timed once on
     the full routing; then plan + dispatch + combine run for about `budget_s`
@@ -804,6 +862,9 @@ def main():
     ap.add_argument("--step-only", action="store_true",
                     help="time the step only: no ceilings, ablations, sweep, secondary section "
                          "or CPU baseline (the counter runs use this)")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="the step and the memory-system ceiling legs only (the stall-counter "
+                         "runs use this)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate", action="store_true",
                     help="run only a plain 1 GiB elementwise copy (scales HBM counters)")
@@ -816,12 +877,17 @@ def main():
     ap.add_argument("--commands", nargs="*", default=[],
                     help="the profiler commands, recorded in the summary")
     ap.add_argument("--bench-log", help="log of the traced run (its JSON line is quoted)")
+    ap.add_argument("--summarize-stalls", nargs=2, metavar="DIR",
+                    help="rocprofv3 csv folders of the two memory-queue counter passes of a "
+                         "--ceilings-only run; writes profiles/stalls_<workload>.md")
     args = ap.parse_args()
-    if args.summarize_pmc or args.summarize_trace:
+    if args.summarize_pmc or args.summarize_trace or args.summarize_stalls:
         import synth
         name = synth.WORKLOADS[synth.workload_id(args.workload)]["name"]
         if args.summarize_pmc:
             summarize_pmc(name, args.summarize_pmc, args.commands)
+        elif args.summarize_stalls:
+            summarize_stalls(name, args.summarize_stalls, args.commands)
         else:
             summarize_trace(name, args.summarize_trace, " ".join(args.commands), args.bench_log)
         return
@@ -855,7 +921,10 @@ def main():
     ceilings = ablations = weights = serving = copy = cpu = secondary = None
     sweep, flat = [], None
     iters = max(10, args.steps // 5)
-    if full:
+    if args.ceilings_only:
+        ceilings = measure_ceilings(moon, ctx, sets[0], nb0, stream, max(3, args.steps))
+        release(moon, ctx, sets)
+    elif full:
         log("[bench] memory-system ceilings")
         ceilings = measure_ceilings(moon, ctx, sets[0], nb0, stream, iters)
         copy = measure_copy(stream)

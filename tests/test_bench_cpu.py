@@ -154,3 +154,39 @@ def test_cpu_baseline_record():
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "GB/s"
     assert rec["value"] > 0 and rec["tokens_per_s"] > 0 and rec["plan_full_ms"] > 0
     assert "the first 64 of the 2048 tokens" in rec["sample"] and ") x 1: plan " in rec["sample"]
+
+
+def test_stall_summary_divides_by_busy_cycles(tmp_path, monkeypatch):
+    """The memory-queue table: per kernel (template arguments dropped, means
+    over launches), request counts, queue levels and credit stalls over the
+    GPU's busy cycles of the same pass."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(bench.PROFILES)
+    K_SCATTER = "void moon::(anonymous namespace)::k_dispatch_scatter<2, true>(moon::Dims, ...)"
+    K_FILL = "(anonymous namespace)::k_fill(unsigned int __vector(4)*, long)"
+
+    def pass_csv(path, values):
+        rows = []
+        for did, (name, cs) in enumerate(values):
+            for c, v in cs.items():
+                rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": c,
+                             "Counter_Value": v})
+        _write_csv(path, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+
+    a = {"TCC_EA0_WRREQ_sum": 400.0, "TCC_EA0_WRREQ_64B_sum": 400.0, "TCC_EA0_RDREQ_sum": 50.0,
+         "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum": 10.0, "GRBM_GUI_ACTIVE": 100.0}
+    b = {"TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum": 30.0, "TCC_TAG_STALL_sum": 20.0,
+         "TCC_EA0_WRREQ_LEVEL_sum": 150000.0, "TCC_EA0_RDREQ_LEVEL_sum": 90000.0,
+         "GRBM_GUI_ACTIVE": 100.0}
+    a2 = dict(a, TCC_EA0_WRREQ_sum=600.0)  # second launch: mean 500 write requests
+    pass_csv(str(tmp_path / "A" / "run_counter_collection.csv"),
+             [(K_SCATTER, a), (K_SCATTER, a2), (K_FILL, a)])
+    pass_csv(str(tmp_path / "B" / "run_counter_collection.csv"),
+             [(K_SCATTER, b), (K_SCATTER, b), (K_FILL, b)])
+    bench.summarize_stalls("wl-test", [str(tmp_path / "A"), str(tmp_path / "B")], ["cmd a"])
+    md = open(os.path.join(bench.PROFILES, "stalls_wl-test.md")).read().splitlines()
+    rows = {ln.split("|")[1].strip(): ln for ln in md if ln.startswith("| k_")}
+    assert set(rows) == {"k_dispatch_scatter", "k_fill"}
+    cells = [c.strip() for c in rows["k_dispatch_scatter"].split("|")[2:-1]]
+    assert cells == ["100", "5.000", "0.500", "1500", "900", "0.300", "0.100", "0.200"]
+    assert "    cmd a" in md
