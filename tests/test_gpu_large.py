@@ -14,6 +14,8 @@ first) and the rows a comparison needs are regenerated on the host:
 * R=16 shape at maxvio 8: the window of the rank with the most slots in
   full, for both dispatch paths, and combine over every token of one source
   rank; the other maxvio levels on sampled rows and tokens.
+* Without route weights (DSv3 in full, R=16 at maxvio 4 sampled): the weight
+  windows stay untouched and combine is the plain K-sum.
 """
 import numpy as np
 import pytest
@@ -64,7 +66,7 @@ class Run:
     """Plan + dispatch + combine of one full-size workload on the GPU, and the
     oracle's plan of the same routing (compared bit for bit)."""
 
-    def __init__(self, moon, dev, config, level, dflags):
+    def __init__(self, moon, dev, config, level, dflags, weighted=True):
         import torch
 
         import synth.gpu as sg
@@ -89,14 +91,18 @@ class Run:
         assert np.array_equal(
             pt.dev_bits(self.hidden.view(R * S, H)[torch.from_numpy(probe).to(dev)]),
             synth.bf16_rows(self.kh, probe, H))
-        w_d = pt.to_dev(wl["w"], dev)
+        # unweighted: dispatch without route weights, plain K-sum combine
+        self.weighted = weighted
+        w_d = pt.to_dev(wl["w"], dev) if weighted else None
         moon.moon_plan(ctx, pt.to_dev(wl["topk"], dev), None, plan)
-        moon.moon_dispatch(ctx, plan, self.hidden, w_d, flags=dflags)
         self.win, self.wwin = moon.window_tensors(ctx)
+        if not weighted:
+            self.wwin.fill_(-3.0)  # must stay untouched
+        moon.moon_dispatch(ctx, plan, self.hidden, w_d, flags=dflags)
         self.out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
         self.wsk = torch.empty((R, S, K), dtype=torch.float32, device=dev)
-        moon.moon_combine(ctx, plan, self.y, self.wwin, moon.MOON_COMBINE_WEIGHTED, self.out,
-                          self.wsk)
+        moon.moon_combine(ctx, plan, self.y, self.wwin,
+                          moon.MOON_COMBINE_WEIGHTED if weighted else 0, self.out, self.wsk)
         self.pidx = torch.empty((R, ctx.B, 2), dtype=torch.int32, device=dev)
         moon.moon_prefetch_index(ctx, plan, self.pidx)
         assert moon.moon_plan_status(plan) == moon.MOON_OK
@@ -113,11 +119,15 @@ class Run:
             f"dup rows {int(ref.dup_counts[:, 1].sum())}")
         assert np.array_equal(self.pidx.cpu().numpy(), oracle.prefetch_index(ref))
         self.src = oracle.row_sources(ref)
-        _, self.ewwin = oracle.dispatch(ref, np.zeros((R, S, 0), np.uint16), wl["w"])
-        # every covered weight-window entry, bit for bit
         cov = self.src != -2
-        assert np.array_equal(self.wwin.cpu().numpy()[cov].view(np.uint32),
-                              self.ewwin[cov].view(np.uint32)), "weight windows differ"
+        if weighted:
+            _, self.ewwin = oracle.dispatch(ref, np.zeros((R, S, 0), np.uint16), wl["w"])
+            # every covered weight-window entry, bit for bit
+            assert np.array_equal(self.wwin.cpu().numpy()[cov].view(np.uint32),
+                                  self.ewwin[cov].view(np.uint32)), "weight windows differ"
+        else:
+            assert bool((self.wwin == -3.0).all()), "dispatch without weights wrote weights"
+            self.ewwin = np.full(R * ctx.NvS, -3.0, np.float32)  # what combine gathers
 
     def close(self, moon):
         moon.moon_plan_destroy(self.plan)
@@ -158,10 +168,10 @@ class Run:
         need = np.unique(pc.decode(dst_tok).reshape(-1))
         yrows = synth.bf16_rows(self.ky, need, H)
         eout, ewsk, acc = oracle.combine_rows(dst_tok, need, yrows, self.ewwin[need],
-                                              weighted=True)
+                                              weighted=self.weighted)
         toks_d = torch.from_numpy(toks).to(self.out.device)
         g_out = pt.dev_bits(self.out.view(R * S, H)[toks_d])
-        absum = pt.abs_sum(dst_tok, need, yrows, self.ewwin[need], True)
+        absum = pt.abs_sum(dst_tok, need, yrows, self.ewwin[need], self.weighted)
         dmax, ndiff = pt.check_combine(g_out, eout, acc, absum, K)
         assert np.array_equal(self.wsk.view(R * S, K)[toks_d].cpu().numpy().view(np.uint32),
                               ewsk.view(np.uint32))
@@ -225,12 +235,32 @@ def test_r16_maxvio8_busiest_window(env, path):
         run.close(moon)
 
 
-@pytest.mark.parametrize("level", [0, 2])
-def test_r16_other_levels_sampled(env, level):
-    """R=16 shape at maxvio about 0 and 2: plan in full, sampled window rows
-    and combine tokens."""
+def test_dsv3_unweighted_every_window_row(env):
+    """DSv3 shape without route weights: the weight windows stay untouched,
+    every covered window row as above, and the plain K-sum combine over every
+    token of source rank 6."""
     moon, dev = env
-    run = Run(moon, dev, "r16-e384-k8", level, 0)
+    run = Run(moon, dev, "dsv3", 0, 0, weighted=False)
+    try:
+        hidden_host = synth.hidden_bf16(run.wl["seed"], run.R, run.S, run.H).reshape(
+            run.R * run.S, run.H)
+        for u in range(run.R):
+            run.check_window(u, hidden_host)
+        del hidden_host
+        toks = np.arange(6 * run.S, 7 * run.S)
+        dmax, ndiff, n = run.check_combine(toks)
+        say(f"   unweighted combine on rank 6's tokens: max|d|={dmax:.3g}, "
+            f"bf16 mismatches {ndiff}/{n}")
+    finally:
+        run.close(moon)
+
+
+@pytest.mark.parametrize("level,weighted", [(0, True), (2, True), (3, False)])
+def test_r16_other_levels_sampled(env, level, weighted):
+    """R=16 shape at maxvio about 0, 2 and 4: plan in full, sampled window
+    rows and combine tokens (maxvio 4 without route weights)."""
+    moon, dev = env
+    run = Run(moon, dev, "r16-e384-k8", level, 0, weighted=weighted)
     try:
         n = run.check_rows(sample_rows(run.rng, run.ref, run.src))
         say(f"   {n} sampled window rows bit-exact")

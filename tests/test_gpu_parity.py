@@ -105,7 +105,7 @@ def test_workload_full_parity(env, config, level, path):
     run_full(moon, dev, wl["topk"], wl["w"], hidden, y, wl["R"], wl["E"], wl["K"], wl["S"],
              wl["H"], wl["B"], wl["P"], label=wl["name"],
              dflags=moon.MOON_DISPATCH_DEDUP_EPILOGUE if path == "epilogue" else 0,
-             weighted=path == "fused" or level % 2 == 0)
+             weighted=level % 2 == 0)
 
 
 def _edge_topk(rng, R, S, K, E, mode):
