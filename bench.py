@@ -220,7 +220,8 @@ def _ceiling_lib():
         lib.moon_ceiling_copy.argtypes = [vp, vp, i64, vp]
         lib.moon_ceiling_write_rows.argtypes = [vp, vp, i64, i32, i32, vp]
         lib.moon_ceiling_read_rows.argtypes = [vp, vp, i64, i32, i32, vp, vp]
-        for f in ("read", "fill", "copy", "write_rows", "read_rows"):
+        lib.moon_ceiling_scatter_cached.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        for f in ("read", "fill", "copy", "write_rows", "read_rows", "scatter_cached"):
             getattr(lib, "moon_ceiling_" + f).restype = ctypes.c_int
         _CEIL = lib
     return _CEIL
@@ -232,6 +233,8 @@ def measure_ceilings(moon, ctx, s, nb, stream, iters):
     of back-to-back launches):
       write_rows  dispatch's stores without its loads (every route's row of
                   the plan's dst, same grid and slice order as dispatch)
+      scatter_cached  dispatch with its token rows served from the last-level
+                  cache (token t stores the row of token t mod 4096)
       read_rows   combine's loads without its stores (the K routed rows of
                   every token, same grid as combine)
       fill / read contiguous non-temporal stores / loads over the windows and
@@ -257,6 +260,10 @@ def measure_ceilings(moon, ctx, s, nb, stream, iters):
     legs = {
         "write_rows": (nb["n_route"] * row, lambda i=0: chk(lib.moon_ceiling_write_rows(
             win.data_ptr(), dst.data_ptr(), ntok, c.K, c.H, st))),
+        "scatter_cached": (nb["n_route"] * row + ntok * row,
+                           lambda i=0: chk(lib.moon_ceiling_scatter_cached(
+                               s.hidden.data_ptr(), win.data_ptr(), dst.data_ptr(), ntok, c.K,
+                               c.H, st))),
         "read_rows": (nb["n_route"] * row, lambda i=0: chk(lib.moon_ceiling_read_rows(
             s.y.data_ptr(), dst.data_ptr(), ntok, c.K, c.H, sink.data_ptr(), st))),
         "fill": (win.numel() * 2, lambda i=0: chk(lib.moon_ceiling_fill(
@@ -626,8 +633,8 @@ STALL_PASSES = [["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_su
                  "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "GRBM_GUI_ACTIVE"],
                 ["TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum", "TCC_TAG_STALL_sum",
                  "TCC_EA0_WRREQ_LEVEL_sum", "TCC_EA0_RDREQ_LEVEL_sum", "GRBM_GUI_ACTIVE"]]
-STALL_KERNELS = ["k_dispatch_scatter", "k_combine", "k_write_rows", "k_read_rows", "k_fill",
-                 "k_read", "k_copy"]
+STALL_KERNELS = ["k_dispatch_scatter", "k_combine", "k_write_rows", "k_scatter_cached",
+                 "k_read_rows", "k_fill", "k_read", "k_copy"]
 
 
 def read_counter_table(d):

@@ -13,6 +13,11 @@
 //   moon_ceiling_read_rows   combine's loads without its stores: for every
 //                            token, 1 KB slices of its K routed rows loaded
 //                            and discarded, the same grid as combine
+//   moon_ceiling_scatter_cached  the one-pass dispatch scatter with its token
+//                            rows served from the cache: token t stores the
+//                            row of token t mod 4096 (58 MB at 14 KB rows,
+//                            resident in the 256 MB last-level cache) to the
+//                            rows of its K routes, same grid and order
 //
 // Loaded values are folded into one word that is stored only when `sink_on`
 // is set (the host passes 0), so the loads cannot be dropped.
@@ -72,6 +77,39 @@ __global__ void __launch_bounds__(256) k_write_rows(u32x4* __restrict__ win,
       for (int k = 0; k < K; ++k) {
         u32x4* dp = win + row_of(__builtin_amdgcn_readlane(dl, k)) * V;
         if (j < V) __builtin_nontemporal_store(v, dp + j);
+      }
+    }
+  }
+}
+
+constexpr int64_t kCachedTokens = 4096;
+
+__global__ void __launch_bounds__(256) k_scatter_cached(const u32x4* __restrict__ hidden,
+                                                        u32x4* __restrict__ win,
+                                                        const int32_t* __restrict__ dst,
+                                                        int64_t ntok, int K, int V) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nsl = (V + kWave * kRowSlice - 1) / (kWave * kRowSlice);
+  const int64_t items = ntok * nsl;
+  const int64_t nw = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t it = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; it < items;
+       it += nw) {
+    const int64_t t = it / nsl;
+    const int c0 = (int)(it - t * nsl) * kWave * kRowSlice;
+    const int dl = lane < K ? dst[t * K + lane] : 0;
+    const u32x4* src = hidden + (t % kCachedTokens) * V;
+    u32x4 buf[kRowSlice];
+#pragma unroll
+    for (int c = 0; c < kRowSlice; ++c) {
+      const int j = c0 + c * kWave + lane;
+      if (j < V) buf[c] = src[j];
+    }
+#pragma unroll
+    for (int c = 0; c < kRowSlice; ++c) {
+      const int j = c0 + c * kWave + lane;
+      for (int k = 0; k < K; ++k) {
+        u32x4* dp = win + row_of(__builtin_amdgcn_readlane(dl, k)) * V;
+        if (j < V) __builtin_nontemporal_store(buf[c], dp + j);
       }
     }
   }
@@ -141,6 +179,20 @@ int moon_ceiling_write_rows(void* win, const int32_t* dst, int64_t ntok, int K, 
   const int nsl = (V + kWave * kRowSlice - 1) / (kWave * kRowSlice);
   hipLaunchKernelGGL(k_write_rows, dim3(grid_for(ntok * nsl, 4, 32768)), dim3(256), 0, s,
                      static_cast<u32x4*>(win), dst, ntok, K, V);
+  return hipGetLastError();
+}
+
+// hidden: [ntok, H] bf16 (only its first min(ntok, 4096) rows are read);
+// win and dst as for moon_ceiling_write_rows.
+int moon_ceiling_scatter_cached(const void* hidden, void* win, const int32_t* dst, int64_t ntok,
+                                int K, int H, hipStream_t s) {
+  if (hidden == nullptr || win == nullptr || dst == nullptr || ntok <= 0 || K < 1 || K > kWave ||
+      H < 8 || H % 8)
+    return hipErrorInvalidValue;
+  const int V = H / 8;
+  const int nsl = (V + kWave * kRowSlice - 1) / (kWave * kRowSlice);
+  hipLaunchKernelGGL(k_scatter_cached, dim3(grid_for(ntok * nsl, 4, 32768)), dim3(256), 0, s,
+                     static_cast<const u32x4*>(hidden), static_cast<u32x4*>(win), dst, ntok, K, V);
   return hipGetLastError();
 }
 
