@@ -466,7 +466,7 @@ moon_status moon_dispatch(moon_ctx* ctx, const moon_comm_plan* plan, const void*
   if (!ctx_ok(ctx) || !plan_ok(plan) || hidden_rsh == nullptr) return MOON_ERR_INVALID_ARG;
   if (plan->ctx != ctx) return MOON_ERR_PLAN_MISMATCH;
   if ((flags & ~(MOON_DISPATCH_FUSED_DUPS | MOON_DISPATCH_DEDUP_EPILOGUE)) != 0 ||
-      (flags & MOON_DISPATCH_FUSED_DUPS && flags & MOON_DISPATCH_DEDUP_EPILOGUE))
+      ((flags & MOON_DISPATCH_FUSED_DUPS) != 0 && (flags & MOON_DISPATCH_DEDUP_EPILOGUE) != 0))
     return MOON_ERR_INVALID_ARG;
   void* hout = hidden_out != nullptr ? hidden_out : ctx->hidden_win;
   float* wout = weights_out != nullptr ? weights_out : ctx->w_win;
