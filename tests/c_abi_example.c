@@ -11,6 +11,9 @@
  *     (x are small integers and K = 4, so every product and sum is exact);
  *   - the prefetch index of every used slot names the slot expert's owner
  *     rank and local row, and (-1, -1) for an unused slot;
+ *   - the plan's own prefetch_index array holds the same;
+ *   - moon_plan_noalloc, given caller-allocated arrays and no context,
+ *     writes the same plan as moon_plan, field for field;
  *   - an expert id out of range sets MOON_ERR_BAD_EXPERT without a launch
  *     error, and a plan of another context is refused on the host.
  * Prints "c abi ok" and exits 0 when every check holds.
@@ -146,6 +149,61 @@ int main(void) {
     const int e = etc[i];
     EXPECT(pidx[2 * i] == (e >= 0 ? e / Eg : -1) && pidx[2 * i + 1] == (e >= 0 ? e % Eg : -1),
            "slot %d: prefetch index (%d, %d) for expert %d", i, pidx[2 * i], pidx[2 * i + 1], e);
+  }
+
+  static int32_t pidx_plan[R * E * 2];
+  HIP_OK(hipMemcpy(pidx_plan, pa.prefetch_index, (size_t)R * B * 2 * 4, hipMemcpyDeviceToHost));
+  EXPECT(memcmp(pidx_plan, pidx, (size_t)R * B * 2 * 4) == 0,
+         "the plan's prefetch_index differs from moon_prefetch_index");
+
+  /* planning without a context into caller-owned arrays */
+  {
+    moon_plan_arrays na = pa;  /* same sizes; fresh device arrays */
+    const size_t n_dst = (size_t)R * S * K, n_eb = (size_t)R * (E + B);
+    na.dst = dev_alloc(n_dst * 4);
+    na.experts_to_copy = dev_alloc((size_t)R * B * 4);
+    na.zero_fill_ranges = dev_alloc(n_eb * 2 * 4);
+    na.remote_stats = dev_alloc((size_t)R * 2 * 4);
+    na.dup_groups = dev_alloc((size_t)R * NvS * 3 * 4);
+    na.dup_loffs = dev_alloc((size_t)R * NvS * 4);
+    na.dup_counts = dev_alloc((size_t)R * 2 * 4);
+    na.cu_seqlens = dev_alloc(n_eb * 4);
+    na.status = dev_alloc(4);
+    na.prefetch_index = dev_alloc((size_t)R * B * 2 * 4);
+    MOON_OK_(moon_plan_noalloc(&cfg, d_topk, NULL, &na, st));
+    HIP_OK(hipStreamSynchronize(st));
+    int32_t status = -1;
+    HIP_OK(hipMemcpy(&status, na.status, 4, hipMemcpyDeviceToHost));
+    EXPECT(status == 0, "moon_plan_noalloc: status word %d", status);
+    struct { const char* name; int32_t* a; int32_t* b; size_t n; } f[] = {
+        {"dst", pa.dst, na.dst, n_dst},
+        {"experts_to_copy", pa.experts_to_copy, na.experts_to_copy, (size_t)R * B},
+        {"zero_fill_ranges", pa.zero_fill_ranges, na.zero_fill_ranges, n_eb * 2},
+        {"remote_stats", pa.remote_stats, na.remote_stats, (size_t)R * 2},
+        {"dup_counts", pa.dup_counts, na.dup_counts, (size_t)R * 2},
+        {"cu_seqlens", pa.cu_seqlens, na.cu_seqlens, n_eb},
+        {"prefetch_index", pa.prefetch_index, na.prefetch_index, (size_t)R * B * 2},
+        {"dup_groups", pa.dup_groups, na.dup_groups, (size_t)R * NvS * 3},
+        {"dup_loffs", pa.dup_loffs, na.dup_loffs, (size_t)R * NvS}};
+    static int32_t ha[R * S * K * 4], hb[R * S * K * 4], cnt[R * 2];
+    HIP_OK(hipMemcpy(cnt, pa.dup_counts, sizeof cnt, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < sizeof f / sizeof f[0]; ++i) {
+      HIP_OK(hipMemcpy(ha, f[i].a, f[i].n * 4, hipMemcpyDeviceToHost));
+      HIP_OK(hipMemcpy(hb, f[i].b, f[i].n * 4, hipMemcpyDeviceToHost));
+      int differ = 0;
+      for (size_t j = 0; j < f[i].n; ++j) {
+        /* duplicate records: the valid prefix of each rank only */
+        if (i == 7 && (int)(j % ((size_t)NvS * 3)) >= cnt[(j / ((size_t)NvS * 3)) * 2] * 3) continue;
+        if (i == 8 && (int)(j % (size_t)NvS) >= cnt[(j / (size_t)NvS) * 2 + 1]) continue;
+        differ += ha[j] != hb[j];
+      }
+      EXPECT(differ == 0, "moon_plan_noalloc: %d entries of %s differ from moon_plan", differ,
+             f[i].name);
+    }
+    int32_t* ptrs[] = {na.dst, na.experts_to_copy, na.zero_fill_ranges, na.remote_stats,
+                       na.dup_groups, na.dup_loffs, na.dup_counts, na.cu_seqlens, na.status,
+                       na.prefetch_index};
+    for (size_t i = 0; i < sizeof ptrs / sizeof ptrs[0]; ++i) HIP_OK(hipFree(ptrs[i]));
   }
 
   /* combine over the dispatched windows: K*x unweighted, x weighted by 1/K */

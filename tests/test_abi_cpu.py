@@ -32,6 +32,18 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
 
 
+def test_ceiling_library_exports_its_legs():
+    """The benchmark's reference kernels load on their own (no GPU needed to
+    resolve the symbols) and refuse bad sizes before any launch."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_balanced_planning_amd", "libmoon_ceiling.so"))
+    for f in ("read", "fill", "copy", "write_rows", "read_rows", "scatter_cached"):
+        assert hasattr(lib, "moon_ceiling_" + f)
+    lib.moon_ceiling_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.moon_ceiling_fill.restype = ctypes.c_int
+    assert lib.moon_ceiling_fill(None, 16, None) != 0       # null pointer
+    assert lib.moon_ceiling_fill(ctypes.c_void_p(16), 24, None) != 0  # not a multiple of 16
+
+
 def test_header_is_plain_c(tmp_path):
     c = tmp_path / "use.c"
     c.write_text('#include "moon.h"\nint main(void){ moon_ctx* c = 0; moon_ctx_destroy(&c);'
