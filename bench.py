@@ -329,29 +329,56 @@ SWEEPS = {"r8-e64-k6": ("r8-e64-k6-skewed", [0, 1, 2, 3]),
           "r16-e384-k8": ("r16-e384-k8", [1, 2, 3, 4])}
 
 # Expert FFN intermediate width H' per workload: DeepSeek-V3's expert width for
-# the DSv3-shaped workload; H/2 (a reading: the pages give none) for r8-e64-k6.
-FFN_WIDTH = {"r8-e64-k6": 1024, "dsv3": 2048}
+# the DSv3-shaped workload and for the R=16 workload, whose hidden width is
+# DeepSeek-V3's too; H/2 for r8-e64-k6 (readings: the pages give none).
+FFN_WIDTH = {"r8-e64-k6": 1024, "dsv3": 2048, "r16-e384-k8": 2048}
 
 
-def measure_weights(moon, ctx, s, stream, iters, hp):
-    """Weight prefetch and gradient reduction for the plan of `s`: gate, up and
-    down tensors [E, H*H'] (bf16 weights, fp32 gradients) and their slots."""
+class WeightBufs:
+    """Expert weights (gate, up, down: [E, H*H'] bf16, seeded) and their slot
+    rows ([R, B, H*H'] bf16) for timing the weight prefetch on any plan of
+    the context."""
+
+    def __init__(self, ctx, hp):
+        import torch
+        import synth
+        import synth.gpu as sg
+        c = ctx.cfg
+        self.ctx, self.hp, self.L = ctx, hp, c.H * hp
+        key = synth.stream_key(12345, 21)
+        self.w = [sg.fill_bf16(torch.empty((c.E, self.L), dtype=torch.bfloat16, device="cuda"),
+                               key, i * c.E * self.L) for i in range(3)]
+        self.sl = [torch.zeros((c.R, ctx.B, self.L), dtype=torch.bfloat16, device="cuda")
+                   for _ in range(3)]
+
+    def prefetch(self, moon, plan, stream, iters):
+        """(µs per call, slots used, experts held, bytes per slot copy, minimum bytes)."""
+        import torch
+        etc = moon.plan_tensors(plan)["experts_to_copy"].cpu()
+        n_used = int((etc >= 0).sum())
+        n_held = int(torch.unique(etc[etc >= 0]).numel())
+        t = time_call(lambda i=0: moon.moon_prefetch_weight(self.ctx, plan, self.w, self.sl,
+                                                          stream=stream), iters, stream)
+        L = self.L
+        return t, n_used, n_held, 3 * n_used * L * 2 * 2, 3 * (n_held + n_used) * L * 2
+
+    def release(self):
+        import torch
+        del self.w, self.sl
+        torch.cuda.empty_cache()
+
+
+def measure_weights(moon, ctx, s, stream, iters, hp, wb=None):
+    """Gradient reduction and weight prefetch for the plan of `s`: gate, up and
+    down tensors [E, H*H'] (bf16 weights, fp32 gradients) and their slots.
+    The reduction's buffers are freed before the prefetch's are taken (or
+    `wb`, already allocated, is used)."""
     import torch
     import synth
     import synth.gpu as sg
     c = ctx.cfg
     L = c.H * hp
-    pt = moon.plan_tensors(s.plan)
-    etc = pt["experts_to_copy"].cpu()
-    n_used = int((etc >= 0).sum())
-    n_held = int(torch.unique(etc[etc >= 0]).numel())
     key = synth.stream_key(12345, 21)
-    w = [sg.fill_bf16(torch.empty((c.E, L), dtype=torch.bfloat16, device="cuda"), key, i * c.E * L)
-         for i in range(3)]
-    sl = [torch.zeros((c.R, ctx.B, L), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
-    t_pw = time_call(lambda i=0: moon.moon_prefetch_weight(ctx, s.plan, w, sl, stream=stream), iters,
-                     stream)
-    del w, sl
     g = [sg.fill_bf16(torch.empty((c.E, L), dtype=torch.bfloat16, device="cuda"), key).float()
          for _ in range(3)]
     sgr = [torch.zeros((c.R, ctx.B, L), dtype=torch.float32, device="cuda") for _ in range(3)]
@@ -359,8 +386,12 @@ def measure_weights(moon, ctx, s, stream, iters, hp):
                      stream)
     del g, sgr
     torch.cuda.empty_cache()
-    pw_bytes = 3 * n_used * L * 2 * 2          # read the expert row, write the slot
-    pw_min = 3 * (n_held + n_used) * L * 2     # each held expert read once, each slot written
+    own = wb is None
+    if own:
+        wb = WeightBufs(ctx, hp)
+    t_pw, n_used, n_held, pw_bytes, pw_min = wb.prefetch(moon, s.plan, stream, iters)
+    if own:
+        wb.release()
     rg_bytes = 3 * (n_held + n_used) * L * 4 * 2  # expert row read+write; slot read+clear
     return {
         "ffn_width": hp, "tensors": 3, "slots_used": n_used, "experts_held": n_held,
@@ -812,8 +843,10 @@ def measure_step(moon, config, dev, stream, steps, warmup):
     return res, ctx, sets, nbs[0]
 
 
-def measure_sweep(moon, ctx, config, base, steps, warmup, stream, dev):
-    """maxvio sweep on the same shapes: the base run, then the skewed levels."""
+def measure_sweep(moon, ctx, config, base, steps, warmup, stream, dev, wb=None, base_plan=None):
+    """maxvio sweep on the same shapes: the base run, then the skewed levels.
+    With `wb`, each level also times the weight prefetch of its plan (the
+    pages stack the planning and weight-prefetch kernels onto dispatch)."""
     import synth
     c = synth.WORKLOADS[synth.workload_id(config)]
     R, S = c["R"], c["S"]
@@ -821,6 +854,14 @@ def measure_sweep(moon, ctx, config, base, steps, warmup, stream, dev):
               "GBps": round(base["value"], 1), "tokens_per_s": base["tokens_per_s"],
               "plan_us": base["plan_us"], "slots_used": base["slots_used"],
               "routes_in_slots": base["routes_in_slots"]}]
+
+    def with_prefetch(point, plan):
+        if wb is not None:
+            t = wb.prefetch(moon, plan, stream, 5)[0]
+            point["prefetch_weight_us"] = round(t, 2)
+            point["ms_per_step_with_weight_prefetch"] = round(point["ms_per_step"] + t * 1e-3, 4)
+
+    with_prefetch(sweep[0], base_plan)
     sc, levels = SWEEPS[config]
     for level in levels:
         target = synth.LEVELS[synth.workload_id(sc)][level]
@@ -839,6 +880,7 @@ def measure_sweep(moon, ctx, config, base, steps, warmup, stream, dev):
                       "combine_us": round(calls4["combine"], 2),
                       "slots_used": b4[0]["slots_used"],
                       "routes_in_slots": b4[0]["routes_in_slots"]})
+        with_prefetch(sweep[-1], s4[0].plan)
         for s in s4:
             moon.moon_plan_destroy(s.plan)
         del s4
@@ -944,13 +986,18 @@ def main():
             kk["frac_of_measured_copy"] = round(kk["achieved"] / ceilings["copy"]["GBps"], 4)
         log("[bench] ablations")
         ablations = measure_ablations(moon, ctx, sets[0], nb0, stream, iters)
+        wb = None
         if config in FFN_WIDTH:
-            log("[bench] weight prefetch and gradient reduction")
+            log("[bench] gradient reduction and weight prefetch")
             weights = measure_weights(moon, ctx, sets[0], stream, max(5, args.steps // 10),
                                       FFN_WIDTH[config])
+            wb = WeightBufs(ctx, FFN_WIDTH[config])
         if not args.no_sweep and config in SWEEPS:
             sweep, flat = measure_sweep(moon, ctx, config, head, max(10, args.steps // 2),
-                                        args.warmup, stream, dev)
+                                        args.warmup, stream, dev, wb, sets[0].plan)
+        if wb is not None:
+            wb.release()
+            del wb
         topk_h, w_h, seed0 = sets[0].topk_h, sets[0].w_h, sets[0].seed
         release(moon, ctx, sets)
         if not args.no_secondary and config != SECONDARY:
