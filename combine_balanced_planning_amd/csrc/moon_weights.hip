@@ -14,15 +14,16 @@
 // of all ranks are one [R, B, row] array, so the remote transfer becomes an
 // HBM copy of whole expert rows.  Bound: HBM bandwidth.
 //
-//   k_slot_index    (gradient reduction) one workgroup: the list of used
-//                   slots (ascending), and
+//   k_slot_index    one workgroup: the list of used slots (ascending), and
 //                   for every expert held by a slot, its slot on each rank
 //                   (experts ascending).  Both lists go to context scratch.
-//   k_prefetch_copy persistent grid over (tensor, slot, 8 KB chunk); items
-//                   of unused slots (-1) end at once, the others copy their
-//                   chunk with cached 16-byte loads and non-temporal stores.
-//                   For more than 64 slots, k_prefetch_copy_listed first
-//                   lists the used slots in LDS and walks only their items.
+//   k_prefetch_copy (up to 64 slots) persistent grid over (tensor, slot,
+//                   8 KB chunk); items of unused slots (-1) end at once, the
+//                   others copy their chunk with cached 16-byte loads and
+//                   non-temporal stores.
+//   k_prefetch_grouped  (more slots) after k_slot_index, a persistent grid
+//                   over (tensor, held expert, 8 KB chunk): the chunk is read
+//                   once and stored to every slot that holds the expert.
 //   k_reduce_grad   persistent grid over (tensor, held expert, 2 KB chunk);
 //                   one wave loads the expert's chunk, adds the matching
 //                   slot chunks in ascending rank order (fp32, a + b), stores
@@ -155,61 +156,48 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// Large slot tables: every workgroup first lists the used slots (ascending,
-// each with its expert) in LDS, then its waves take (tensor, used slot,
-// chunk) items of a grid-wide stride, so no item falls on an unused slot (at
-// 256 slots of which 7 are used this cut the DSv3-shaped prefetch from 246
-// to 195 us; walking every slot stays faster up to 64 slots).
+// Large slot tables: a work item is one wave on an 8 KB chunk of one held
+// expert's row (the slot index lists the held experts and, per expert, its
+// slot on every rank); the chunk is read once, with non-temporal loads, and
+// stored to every slot that holds the expert.  Measured against one copy per
+// used slot (µs): R=16 shape, 15 slots / 6 experts of 3 x 29 MB rows, 367
+// against 426; DSv3 shape, 7 / 5, 201 against 205.  Up to 64 slots the
+// per-slot copy without the index launch stays faster (r8-e64-k6: 23.5
+// against 26.1).
 __global__ void __launch_bounds__(kThreads)
-    k_prefetch_copy_listed(Dims d, PlanArrays pa, TensorArgs ta) {
-  extern __shared__ int used[];  // [R*B] slot | expert << 16, used slots first
-  __shared__ int wave_tot[kWavesPerBlock];
-  if (pa.status[0] != 0) return;  // (uniform: before any barrier)
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int nslots = d.R * d.B;
-  int nused = 0;
-  for (int s0 = 0; s0 < nslots; s0 += kThreads) {
-    const int slot = s0 + threadIdx.x;
-    const int e = slot < nslots ? pa.etc[slot] : -1;
-    const uint64_t b = __ballot(e >= 0);
-    if (lane == 0) wave_tot[w] = __popcll(b);
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int i = 0; i < kWavesPerBlock; ++i) {
-      const int c = wave_tot[i];
-      before += i < w ? c : 0;
-      all += c;
-    }
-    if (e >= 0) used[nused + before + __popcll(b & ((1ull << lane) - 1ull))] = slot | (e << 16);
-    nused += all;
-    __syncthreads();  // the counts are rewritten by the next round; the list is complete
-  }
-  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + w;
+    k_prefetch_grouped(Dims d, PlanArrays pa, SlotIndex si, TensorArgs ta) {
+  if (pa.status[0] != 0) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n_act = si.counts[1];
+  const int64_t wave = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   for (int t = 0; t < ta.n; ++t) {
     const int64_t V = ta.vecs[t];
     const int64_t nch = (V + kWave * kCopyVec - 1) / (kWave * kCopyVec);
-    const int64_t items = (int64_t)nused * nch;
+    const int64_t items = (int64_t)n_act * nch;
     for (int64_t it = wave; it < items; it += nwaves) {
-      const int k = (int)(it / nch);
-      const int64_t c0 = (it - (int64_t)k * nch) * kWave * kCopyVec;
-      const int pk = used[k];
-      const int slot = pk & 0xFFFF, e = pk >> 16;
+      const int a = (int)(it / nch);
+      const int64_t c0 = (it - (int64_t)a * nch) * kWave * kCopyVec;
+      const int e = si.act_e[a];
+      // lane u < R: the slot expert e holds on rank u (-1 if none)
+      const int my_slot = lane < d.R ? si.act_match[a * d.R + lane] : -1;
       const u32x4* sp = ta.src[t] + (int64_t)e * V;
-      u32x4* dp = ta.dst[t] + (int64_t)slot * V;
       u32x4 buf[kCopyVec];
 #pragma unroll
       for (int c = 0; c < kCopyVec; ++c) {
         const int64_t j = c0 + c * kWave + lane;
-        if (j < V) buf[c] = kCopyNtLoad ? __builtin_nontemporal_load(sp + j) : sp[j];
+        if (j < V) buf[c] = __builtin_nontemporal_load(sp + j);
       }
+      uint64_t held = __ballot(my_slot >= 0);
+      while (held != 0) {
+        const int u = __builtin_ctzll(held);
+        held &= held - 1;
+        const int j_slot = __builtin_amdgcn_readlane(my_slot, u);
+        u32x4* dp = ta.dst[t] + ((int64_t)u * d.B + j_slot) * V;
 #pragma unroll
-      for (int c = 0; c < kCopyVec; ++c) {
-        const int64_t j = c0 + c * kWave + lane;
-        if (j < V) {
-          if (kCopyNtStore) __builtin_nontemporal_store(buf[c], dp + j);
-          else dp[j] = buf[c];
+        for (int c = 0; c < kCopyVec; ++c) {
+          const int64_t j = c0 + c * kWave + lane;
+          if (j < V) __builtin_nontemporal_store(buf[c], dp + j);
         }
       }
     }
@@ -316,16 +304,16 @@ TensorArgs tensor_args(int n, const void* const* src, void* const* dst, const in
 hipError_t launch_prefetch_weight(const Dims& d, const PlanArrays& pa, const SlotIndex& si, int n,
                                   const void* const* experts, void* const* slots,
                                   const int64_t* row_bytes, hipStream_t s) {
-  (void)si;  // the copy lists the used slots itself; only the reduction needs the index
   if (d.B == 0) return hipSuccess;
   const TensorArgs ta = tensor_args(n, experts, slots, row_bytes);
   const int blocks = grid_for(d, ta, kCopyVec, kCopyBlocks);
   if (d.R * d.B <= kWave) {
     hipLaunchKernelGGL(k_prefetch_copy, dim3(blocks), dim3(kThreads), 0, s, d, pa, ta);
-  } else {
-    const size_t lds = (size_t)d.R * d.B * sizeof(int);  // <= kMaxSlotsTotal ints
-    hipLaunchKernelGGL(k_prefetch_copy_listed, dim3(blocks), dim3(kThreads), lds, s, d, pa, ta);
+    return hipGetLastError();
   }
+  hipError_t e = launch_index(d, pa, si, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_prefetch_grouped, dim3(blocks), dim3(kThreads), 0, s, d, pa, si, ta);
   return hipGetLastError();
 }
 

@@ -239,8 +239,9 @@ typedef struct {
  * used slot j of every rank u, slots[u][j] <- experts[experts_to_copy[u][j]]
  * (the expert id names its owning rank and rank-local row); unused (-1)
  * slots are not written.  n_tensors in [1, 8]: gate, up, down and, when
- * present, their scales.  Asynchronous on `stream`; reads only the plan
- * (no context scratch).  A plan whose device status is not OK writes
+ * present, their scales.  Asynchronous on `stream`; uses context scratch
+ * (the list of held experts and their slots), so calls on one context are
+ * ordered on one stream.  A plan whose device status is not OK writes
  * nothing. */
 moon_status moon_prefetch_weight(moon_ctx* ctx, const moon_comm_plan* plan,
                                  const moon_weight_tensor* tensors, int32_t n_tensors,

@@ -141,11 +141,13 @@ def test_reduce_grad_small(env, case):
         moon.moon_ctx_destroy(ctx)
 
 
-def test_weights_skip_on_bad_plan(env):
-    """A plan whose device status is an error writes nothing."""
+@pytest.mark.parametrize("R,E,B", [(2, 8, 4), (8, 64, 16)], ids=["8-slots", "128-slots"])
+def test_weights_skip_on_bad_plan(env, R, E, B):
+    """A plan whose device status is an error writes nothing (the per-slot
+    copy up to 64 slots, the grouped copy beyond)."""
     import torch
     moon, dev = env
-    R, E, K, S, B, P = 2, 8, 2, 32, 4, 4
+    K, S, P = 2, 32, 4
     topk = np.zeros((R, S, K), np.int32)
     topk[1, 3, 1] = E  # out of range
     ctx = moon.moon_ctx_create(R, E, K, S, 8, B, P)
