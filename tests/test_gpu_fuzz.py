@@ -1,9 +1,9 @@
 """Seeded random shapes through the whole path against the oracle, with
 longer token ranges than the random-shape parity cases (up to 3000 tokens per
 rank, so the planner runs up to its 256 tiles and the duplicate look-back
-spans many of them), narrow rows, every routing mode and, in half of the
-cases, the tokens_per_expert check.  MOON_FUZZ_CASES sets the number of
-seeds (default 100)."""
+spans many of them), narrow rows, every routing mode, both dispatch paths
+and, in half of the cases, the tokens_per_expert check.  MOON_FUZZ_CASES
+sets the number of seeds (default 100)."""
 import os
 
 import numpy as np
@@ -65,4 +65,5 @@ def test_fuzz_shapes(i):
     y = synth.bf16_normal(int(rng.integers(1 << 62)), 0, R * ref.NvS * H).reshape(
         R * ref.NvS, H)
     tg.run_full(moon, dev, topk, w, hidden, y, R, E, K, S, H, B, P, label=label,
-                weighted=bool(i % 2), tpe=tpe)
+                weighted=bool(i % 2), tpe=tpe,
+                dflags=moon.MOON_DISPATCH_DEDUP_EPILOGUE if i % 4 >= 2 else 0)
