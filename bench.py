@@ -982,6 +982,18 @@ def main():
             ceilings["write_rows"]["us"] / k["k_dispatch_scatter"]["avg_launch_us"], 4)
         k["k_combine"]["read_rows_us_over_launch_us"] = round(
             ceilings["read_rows"]["us"] / k["k_combine"]["avg_launch_us"], 4)
+        # Sum of the parts, each at the rate the memory system gives it alone:
+        # dispatch = its token-row reads at the contiguous read rate + the
+        # rest (route rows, padding, weights) at the row-write rate; combine
+        # = its output at the contiguous fill rate + the rest (route rows,
+        # dst, weights) at the row-read rate.
+        rate = {n: v["bytes"] / v["us"] for n, v in ceilings.items()}  # bytes per µs
+        tok_bytes = 2 * head["H"] * head["R"] * head["S"]
+        t_d = tok_bytes / rate["read"] + (nb0["dispatch"] - tok_bytes) / rate["write_rows"]
+        t_c = tok_bytes / rate["fill"] + (nb0["combine"] - tok_bytes) / rate["read_rows"]
+        for kn, t in (("k_dispatch_scatter", t_d), ("k_combine", t_c)):
+            k[kn]["sum_of_parts_us"] = round(t, 2)
+            k[kn]["sum_of_parts_over_launch_us"] = round(t / k[kn]["avg_launch_us"], 4)
         for kk in k.values():
             kk["frac_of_measured_copy"] = round(kk["achieved"] / ceilings["copy"]["GBps"], 4)
         log("[bench] ablations")
