@@ -11,9 +11,10 @@ first) and the rows a comparison needs are regenerated on the host:
   full, for the default one-pass dispatch and for the pages' two-pass
   structure (whose epilogue reads the primaries with non-temporal loads at
   this size); combine over every token of one source rank.
-* R=16 shape at maxvio 8: the window of the rank with the most slots in
-  full, for both dispatch paths, and combine over every token of one source
-  rank; the other maxvio levels on sampled rows and tokens.
+* R=16 shape at maxvio 8: every covered row of all sixteen rank windows
+  (one-pass dispatch) and the window of the rank with the most slots (the
+  two-pass path), and combine over every token of one source rank; the other
+  maxvio levels on sampled rows and tokens.
 * Without route weights (DSv3 in full, R=16 at maxvio 4 sampled): the weight
   windows stay untouched and combine is the plain K-sum.
 """
@@ -206,25 +207,33 @@ def test_dsv3_every_window_row(env, path):
 
 
 @pytest.mark.parametrize("path", ["fused", "epilogue"])
-def test_r16_maxvio8_busiest_window(env, path):
-    """R=16 shape at maxvio 8 (half the tokens inside one home rank): the
-    window of the rank with the most slots compared row for row, then a
-    sample of the others; combine over every token of source rank 0."""
+def test_r16_maxvio8_windows(env, path):
+    """R=16 shape at maxvio 8 (half the tokens inside one home rank): with
+    the default one-pass dispatch every covered row of all sixteen rank
+    windows, with the two-pass path the window of the rank with the most
+    slots, compared row for row (then a sample of all ranks); combine over
+    every token of source rank 0."""
     moon, dev = env
     run = Run(moon, dev, "r16-e384-k8", 4, _flags(moon, path))
     try:
-        u = int(np.argmax(run.ref.remote_stats[:, 0]))
         NvS, K = run.ctx.NvS, run.K
-        s = run.src[u * NvS:(u + 1) * NvS]
-        toks = np.unique(s[s >= 0] // K)  # tokens routed to rank u
-        rows = synth.bf16_rows(run.kh, toks, run.H)
-        hidden_host = np.zeros((run.R * run.S, run.H), np.uint16)
-        hidden_host[toks] = rows
-        del rows
-        r, p = run.check_window(u, hidden_host)
+        if path == "fused":
+            ranks = list(range(run.R))
+            hidden_host = synth.hidden_bf16(run.wl["seed"], run.R, run.S, run.H).reshape(
+                run.R * run.S, run.H)
+        else:
+            ranks = [int(np.argmax(run.ref.remote_stats[:, 0]))]
+            s = run.src[ranks[0] * NvS:(ranks[0] + 1) * NvS]
+            toks = np.unique(s[s >= 0] // K)  # tokens routed to that rank
+            hidden_host = np.zeros((run.R * run.S, run.H), np.uint16)
+            hidden_host[toks] = synth.bf16_rows(run.kh, toks, run.H)
+        tot_r = tot_p = 0
+        for u in ranks:
+            r, p = run.check_window(u, hidden_host)
+            tot_r, tot_p = tot_r + r, tot_p + p
         del hidden_host
-        say(f"   rank {u} ({int(run.ref.remote_stats[u, 0])} slots): {r} routed rows from "
-            f"{toks.shape[0]} tokens, {p} padding rows bit-exact")
+        say(f"   ranks {ranks if len(ranks) < 4 else 'all'}: {tot_r} routed rows, {tot_p} "
+            f"padding rows bit-exact")
         n = run.check_rows(sample_rows(run.rng, run.ref, run.src))
         say(f"   {n} sampled rows of all ranks bit-exact")
         toks = np.arange(0, run.S)
