@@ -100,3 +100,42 @@ def test_status_strings(moon):
     for s in range(0, -12, -1):
         assert moon.moon_status_str(s) != "unknown status"
     assert moon.moon_status_str(-99) == "unknown status"
+
+
+def test_noalloc_planning_validates_on_the_host(moon):
+    """moon_plan_noalloc refuses missing arguments, a bad configuration and
+    an array description that does not match the configuration before it
+    touches the GPU."""
+    lib = moon._lib
+    pa = moon.moon_plan_arrays()
+    topk = ctypes.c_void_p(256)
+    cfg = moon.moon_config(2, 8, 2, 64, 128, 0, 8, 0)
+    assert lib.moon_plan_noalloc(None, topk, None, ctypes.byref(pa), None) == \
+        moon.MOON_ERR_INVALID_ARG
+    assert lib.moon_plan_noalloc(ctypes.byref(cfg), topk, None, None, None) == \
+        moon.MOON_ERR_INVALID_ARG
+    bad = moon.moon_config(3, 8, 2, 64, 128, 0, 8, 0)  # E % R != 0
+    assert lib.moon_plan_noalloc(ctypes.byref(bad), topk, None, ctypes.byref(pa), None) == \
+        moon.MOON_ERR_TOPOLOGY
+    shapes, NvS, B = moon.plan_array_shapes(2, 8, 2, 64, 0, 8)
+    for i, k in enumerate(shapes):
+        setattr(pa, k, ctypes.c_void_p(4096 * (i + 1)))
+    pa.N, pa.R, pa.E, pa.B, pa.NvS, pa.K = 64 * 2, 2, 8, B, NvS + 8, 2  # wrong capacity
+    assert lib.moon_plan_noalloc(ctypes.byref(cfg), topk, None, ctypes.byref(pa), None) == \
+        moon.MOON_ERR_INVALID_ARG
+    pa.NvS = NvS
+    pa.dup_loffs = ctypes.c_void_p(4098)  # misaligned
+    assert lib.moon_plan_noalloc(ctypes.byref(cfg), topk, None, ctypes.byref(pa), None) == \
+        moon.MOON_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("R,E,K,S,B,P", [(2, 8, 2, 64, 0, 8), (8, 64, 6, 2048, 8, 16),
+                                         (16, 384, 8, 8192, 24, 128), (4, 16, 3, 7, 1, 5)])
+def test_plan_array_shapes_capacity(moon, R, E, K, S, B, P):
+    """The binding sizes no-alloc plan arrays with the capacity the oracle
+    derives from the same configuration."""
+    import oracle
+    shapes, NvS, Bx = moon.plan_array_shapes(R, E, K, S, B, P)
+    assert Bx == (B if B > 0 else E // R)
+    assert NvS == oracle.nvs(R, E, K, S, Bx, P)
+    assert shapes["dup_groups"] == (R, NvS, 3) and shapes["prefetch_index"] == (R, Bx, 2)
