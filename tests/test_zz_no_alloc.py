@@ -5,7 +5,9 @@ Calls in a row, each smaller than the one before, on one GPU's shared
 scratch block: every plan array must equal the plan of moon_plan (context
 scratch) on the same routing bit for bit (duplicate records on their valid
 prefixes), and the oracle's.  Shapes whose scratch exceeds the block, and
-array descriptions that do not match the configuration, are refused."""
+array descriptions that do not match the configuration, are refused.  The
+call captured in a HIP graph replans whatever routing its captured input
+buffer holds, replay after replay."""
 import numpy as np
 import pytest
 
@@ -134,3 +136,55 @@ def test_refusals(env):
         with pytest.raises(moon.MoonError) as ei:
             moon.moon_plan_noalloc(R, E, K, S, H, B, P, topk, None, arrays)
         assert ei.value.status == moon.MOON_ERR_UNSUPPORTED
+
+
+def test_noalloc_plan_in_a_graph(env):
+    """The no-alloc planner captured in a HIP graph (what it is for): the
+    graph replans whatever routing sits in its captured input buffer; every
+    replay, with eager planning calls on the same GPU between replays, equals
+    moon_plan on that routing."""
+    moon, dev = env
+    import torch
+    wl = synth.workload("r8-e64-k6")
+    R, E, K, S, H, B, P = (wl[k] for k in ("R", "E", "K", "S", "H", "B", "P"))
+    routings = [wl["topk"], synth.workload("r8-e64-k6-skewed", 3)["topk"]]
+    topk_buf = pt.to_dev(routings[0], dev)
+    arrays, _ = _arrays(moon, dev, R, E, K, S, B, P)
+    other, _ = _arrays(moon, dev, R, E, K, S, B, P)
+    st = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(st):
+        moon.moon_plan_noalloc(R, E, K, S, H, B, P, topk_buf, None, arrays, stream=st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        moon.moon_plan_noalloc(R, E, K, S, H, B, P, topk_buf, None, arrays,
+                               stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    plan = moon.moon_plan_create(ctx)
+    try:
+        exp = []
+        for tk in routings:
+            moon.moon_plan(ctx, pt.to_dev(tk, dev), None, plan)
+            assert moon.moon_plan_status(plan) == moon.MOON_OK
+            exp.append(pt.gpu_plan_arrays(plan))
+        say("[case] no-alloc plan in a graph: 6 replays")
+        for r in range(6):
+            i = r % 2
+            topk_buf.copy_(pt.to_dev(routings[i], dev))
+            for v in arrays.values():
+                v.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            # an eager no-alloc call on the other routing between replays
+            moon.moon_plan_noalloc(R, E, K, S, H, B, P, pt.to_dev(routings[1 - i], dev), None,
+                                   other)
+            torch.cuda.synchronize()
+            got = {k: v.cpu().numpy() for k, v in arrays.items()}
+            assert int(got["status"][0]) == 0
+            _compare(got, exp[i], R)
+            _compare({k: v.cpu().numpy() for k, v in other.items()}, exp[1 - i], R)
+        del g
+    finally:
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
