@@ -108,6 +108,20 @@ def test_workload_full_parity(env, config, level, path):
              weighted=level % 2 == 0)
 
 
+@pytest.mark.parametrize("config", ["tiny", "r8-e64-k6"])
+@pytest.mark.parametrize("path", ["fused", "epilogue"])
+def test_workload_unweighted_full_parity(env, config, path):
+    """The same two workloads without route weights: dispatch leaves the
+    weight window alone and combine is the plain K-sum."""
+    moon, dev = env
+    wl, hidden, y = workload_inputs(config, 0)
+    say(f"[workload] {wl['name']} unweighted {path}")
+    run_full(moon, dev, wl["topk"], None, hidden, y, wl["R"], wl["E"], wl["K"], wl["S"],
+             wl["H"], wl["B"], wl["P"], label=wl["name"] + " unweighted",
+             dflags=moon.MOON_DISPATCH_DEDUP_EPILOGUE if path == "epilogue" else 0,
+             weighted=False)
+
+
 def _edge_topk(rng, R, S, K, E, mode):
     if mode == "uniform":
         return np.stack([rng.permutation(E)[:K] for _ in range(R * S)]).reshape(R, S, K).astype(
