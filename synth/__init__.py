@@ -311,11 +311,13 @@ def y_bf16(seed, rows, H):
 
 
 def serving_capacity(n_max, min_capacity, max_tokens):
-    """Smallest power of two >= n_max, clamped to [min_capacity, max_tokens]."""
-    if n_max >= max_tokens:
-        return max_tokens
-    cap = 1 << max(n_max - 1, 0).bit_length()
-    return min(max(cap, min_capacity), max_tokens)
+    """Padded capacity of a serving step: the least power of two that is at
+    least n_max (1 for an empty step), raised to min_capacity and capped at
+    max_tokens."""
+    p = 1
+    while p < n_max:
+        p *= 2
+    return min(max_tokens, max(min_capacity, p))
 
 
 def serving_workload(level, n_tok=None):

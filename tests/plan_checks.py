@@ -9,8 +9,8 @@ plan, and run on plans from either the CPU oracle or the GPU library:
   padded end offsets (Visual Guide, Buffer(...) token_padding; dispatch table,
   cu_seqlens);
 * unused prefetch slots are -1 and empty (Visual Guide, prefetch_weight);
-* a rank duplicates experts from at most one remote home rank (README, "How to
-  set B");
+* every slot expert of a rank is homed on one and the same other rank
+  (README, "How to set B");
 * positive dst entries are primaries, negative ones local duplicates, and the
   duplicate records list exactly the duplicates (Visual Guide, combine and
   MoonEPCommPlan).
