@@ -3,7 +3,7 @@
 //
 // ("MoonEP Public API Visual Guide", Buffer.prefetch_weight: each used slot j
 //  of rank u receives the weights of expert experts_to_copy[u][j], found
-//  through its owning rank and rank-local row; the same copy for gate, up,
+//  through its home rank and its row there; the same copy for gate, up,
 //  down and optional scales.  Buffer.reduce_grad: each expert's own fp32
 //  gradient is the seed, the slot gradients of every rank that held the
 //  expert are added, the sum goes back to the expert's row and the consumed

@@ -237,7 +237,7 @@ typedef struct {
 
 /* Weight prefetch (Guide, Buffer.prefetch_weight): for every tensor and every
  * used slot j of every rank u, slots[u][j] <- experts[experts_to_copy[u][j]]
- * (the expert id names its owning rank and rank-local row); unused (-1)
+ * (the expert id names its home rank and its row there); unused (-1)
  * slots are not written.  n_tensors in [1, 8]: gate, up, down and, when
  * present, their scales.  Asynchronous on `stream`; uses context scratch
  * (the list of held experts and their slots), so calls on one context are

@@ -161,8 +161,9 @@ int32_t orc_nvs(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B, int32_t P
 }
 
 // Balance (reading): every rank must end with exactly C routes (README,
-// Perfect balance), and a rank may take overflow from at most one remote
-// home rank, so at most E/R slot experts (README, How to set B).
+// Perfect balance), and the overflow a rank takes in must all come from a
+// single other rank's home experts, so it needs at most E/R slots (README,
+// How to set B).
 // Under-loaded ranks are served in ascending rank order from the lowest
 // over-loaded rank; a rank keeps its own routes first (home-first); a donor
 // pushed below C becomes a receiver itself and joins the back of the queue.
@@ -224,8 +225,8 @@ int32_t orc_plan(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B, int32_t 
   const int64_t NR = (int64_t)R * S * K;  // all routes, global order (r, s, k)
 
   // ---- Histogram: routes per (source rank, expert) and per expert.
-  // (Visual Guide, dispatch table: tokens_per_expert is the source-rank
-  //  histogram used by planning.)  Ids outside [0, E) are an error: the
+  // (Visual Guide, dispatch table: the planner's input tokens_per_expert is
+  //  this count per source rank.)  Ids outside [0, E) are an error: the
   // planner has no sentinel id.
   std::vector<int64_t> cnt((size_t)R * E, 0), T(E, 0);
   for (int64_t i = 0; i < NR; ++i) {
@@ -545,8 +546,9 @@ int32_t orc_combine_prologue_rows(int32_t n, int32_t K, int32_t H, int32_t NvS,
   return ST_OK;
 }
 
-// Prefetch index: a slot's global expert id splits into its owning rank and
-// its row on that rank (Visual Guide, Buffer.prefetch_weight).
+// Prefetch index: a slot's global expert id names the rank that homes the
+// expert and the expert's row among that rank's experts (Visual Guide,
+// Buffer.prefetch_weight).
 int32_t orc_prefetch_index(int32_t R, int32_t E, int32_t B, const int32_t* etc, int32_t* out) {
   if (R <= 0 || E % R != 0) return ST_INVALID;
   int Eg = E / R;
