@@ -125,6 +125,7 @@ moon_status make_dims(const moon_config* c, Dims* d) {
   d->tbits = bits_for(d->ctok);
   d->ebits = bits_for(c->E);
   d->rbits = bits_for(c->R);
+  d->ncu = cus > 0 ? cus : 256;
   return MOON_OK;
 }
 

@@ -7,14 +7,19 @@
 //  entries.  A prologue may first fold the duplicate rows of a token on one
 //  destination rank into that rank's primary row in fp32.)
 //
-// k_combine: a work item is one wave on a slice of 64 vectors (512 bf16) of
-// one token's row.  Lanes 0..K-1 decode the token's K dst entries (both
-// signs: every route owns its row) and fetch the K route weights; the loop
-// over k reads two routed slices at a time with 16-byte loads, widens bf16
-// to fp32 and accumulates c_k * y in ascending k with a separate multiply
-// and add (the library is built with -ffp-contract=off), then rounds once to
-// bf16 (nearest, ties to even).  Bound: HBM bandwidth (K row reads + one row
-// write per token).
+// k_combine_staged (the default): a workgroup of 16 waves owns a run of
+// consecutive tokens whose output rows fill about 140 KB of LDS.  A work item
+// is one wave on a slice of 64 vectors (512 bf16) of one token's row.  Lanes
+// 0..K-1 decode the token's K dst entries (both signs: every route owns its
+// row) and fetch the K route weights; the loop over k reads two routed slices
+// at a time with 16-byte loads, widens bf16 to fp32 and accumulates c_k * y
+// in ascending k with a separate multiply and add (the library is built with
+// -ffp-contract=off), then rounds once to bf16 (nearest, ties to even) into
+// LDS.  When all of its tokens are summed, the workgroup writes their rows as
+// one contiguous run.  Bound: HBM bandwidth (K row reads + one row write per
+// token); the long output runs write faster between the gathers than one
+// 1 KB store per slice does.  k_combine is the same sum stored slice by
+// slice, used by the duplicate-prologue path.
 //
 // With the prologue, k_combine_fold first sums, per duplicate group and
 // slice, the primary row and its duplicate rows (ascending k, c_k * y in
@@ -31,11 +36,22 @@ namespace {
 constexpr int kWavesPerBlock = 16;  // one workgroup = 16 waves (chosen by a sweep of 4, 8, 16)
 constexpr int kThreads = kWavesPerBlock * kWave;
 constexpr int kUnroll = 2;  // rows in flight per wave in the prologue fold
-constexpr int kCombineSliceVec = 1;  // 16-byte vectors per lane in a gather slice
 constexpr int kCombineUnroll = 2;    // routed rows loaded before they are summed
 constexpr bool kCombineNtLoad = true;   // routed rows are read once: non-temporal loads
 constexpr bool kCombineNtStore = true;  // outputs are not read back here: non-temporal stores
 constexpr int kFoldBlocks = 8192;  // persistent grid of the prologue
+// Staged gather: one 16-wave workgroup per compute unit (its LDS block takes
+// most of the unit's 160 KB), tokens per workgroup = the rows that fit.
+constexpr int kStageThreads = 1024;
+constexpr int kStageVec = 140 * 1024 / 16;  // 16-byte vectors of staged output
+constexpr int kStageRoutes = 2048;          // routes whose dst and weight a workgroup stages
+constexpr int kStageBatch = 8;              // vectors a thread moves per write step
+constexpr int kStageUnroll = 8;             // routed rows loaded before they are summed
+// A staged workgroup's fixed cost beside its tokens, in tokens' worth of
+// time (fitted on MI355X: it makes 10 tokens of 14 KB rows per workgroup
+// beat 8 and 9 at 32768 and 131072 tokens, and 32 beat 35 at 16384 tokens of
+// 4 KB rows).
+constexpr int kStageFixed = 3;
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -117,31 +133,16 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-template <bool PROLOGUE, int SV, int KU>
-__global__ void __launch_bounds__(kThreads)
-    k_combine(Dims d, PlanArrays pa, const u32x4* __restrict__ y, const float* __restrict__ wnvs,
-              int weighted, const u32x4* __restrict__ fold, u32x4* __restrict__ out,
-              float* __restrict__ wsk) {
-  constexpr int SW = kWave * SV;  // vectors per slice
-  const int lane = threadIdx.x & (kWave - 1);
+// The sum of one token slice (64 vectors, one per lane: j = slice*64 + lane)
+// over the token's K routes; dl/gl/wl are lane k's dst entry, its row and its
+// route weight (lanes < K).  Routed slices are loaded KU at a time; fp32
+// separate multiply and add in ascending k; one round to bf16.  Returns this
+// lane's rounded vector (meaningful where j < V).
+template <bool PROLOGUE, int KU>
+__device__ __forceinline__ u32x4 combine_slice(const Dims& d, const u32x4* __restrict__ y,
+                                               const u32x4* __restrict__ fold, int weighted,
+                                               int lane, int dl, int gl, float wl, int j) {
   const int V = d.H / 8;
-  const int nsl = (V + SW - 1) / SW;
-  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-  if (item >= (int64_t)d.R * d.S * nsl) return;
-  const int64_t t = item / nsl;
-  const int sl = (int)(item - t * nsl);
-  const int j0 = sl * SW + lane;  // this lane's vectors: j0 + c * kWave
-  int gl = 0, dl = 0;
-  float wl = 0.0f;
-  // The dst entries are read before the plan's status is checked, so the two
-  // loads overlap; nothing read before the check is used unless it is zero.
-  if (lane < d.K) dl = pa.dst[t * d.K + lane];
-  if (pa.status[0] != 0) return;
-  if (lane < d.K) {
-    gl = (int)dst_global_row(dl);
-    if (wnvs != nullptr) wl = wnvs[gl];
-    if (wsk != nullptr && sl == 0) wsk[t * d.K + lane] = wl;
-  }
   // With the prologue: lane k is a folded primary when a duplicate route of
   // the token has the same destination rank; duplicates are skipped.
   int folded = 0;
@@ -154,13 +155,11 @@ __global__ void __launch_bounds__(kThreads)
     }
     folded = folded && dl >= 0 && lane < d.K;
   }
-  float acc[SV][8];
+  float acc[8];
 #pragma unroll
-  for (int c = 0; c < SV; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
   for (int k0 = 0; k0 < d.K; k0 += KU) {
-    u32x4 buf[KU][SV];
+    u32x4 buf[KU];
     float ck[KU];
     bool use[KU];
 #pragma unroll
@@ -178,35 +177,125 @@ __global__ void __launch_bounds__(kThreads)
         }
       }
       const u32x4* row = src + (int64_t)G * V;
-#pragma unroll
-      for (int c = 0; c < SV; ++c) {
-        const int j = j0 + c * kWave;
-        if (j < V && use[uu])
-          buf[uu][c] = kCombineNtLoad ? __builtin_nontemporal_load(row + j) : row[j];
-      }
+      if (j < V && use[uu])
+        buf[uu] = kCombineNtLoad ? __builtin_nontemporal_load(row + j) : row[j];
     }
 #pragma unroll
     for (int uu = 0; uu < KU; ++uu) {
       if (!use[uu]) continue;
 #pragma unroll
-      for (int c = 0; c < SV; ++c)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[c][2 * q + 0] = acc[c][2 * q + 0] + ck[uu] * bf16_lo(buf[uu][c][q]);
-          acc[c][2 * q + 1] = acc[c][2 * q + 1] + ck[uu] * bf16_hi(buf[uu][c][q]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q + 0] = acc[2 * q + 0] + ck[uu] * bf16_lo(buf[uu][q]);
+        acc[2 * q + 1] = acc[2 * q + 1] + ck[uu] * bf16_hi(buf[uu][q]);
+      }
     }
   }
+  u32x4 v;
 #pragma unroll
-  for (int c = 0; c < SV; ++c) {
-    const int j = j0 + c * kWave;
-    if (j < V) {
-      u32x4 v;
+  for (int q = 0; q < 4; ++q) v[q] = bf16_rne(acc[2 * q]) | (bf16_rne(acc[2 * q + 1]) << 16);
+  return v;
+}
+
+// Lanes < K: the token's dst entry, its row, its route weight; slice 0 also
+// writes the weight gather w_sk.
+__device__ __forceinline__ void combine_routes(const Dims& d, const float* __restrict__ wnvs,
+                                               float* __restrict__ wsk, int64_t t, int sl,
+                                               int lane, int dl, int& gl, float& wl) {
+  gl = 0;
+  wl = 0.0f;
+  if (lane < d.K) {
+    gl = (int)dst_global_row(dl);
+    if (wnvs != nullptr) wl = wnvs[gl];
+    if (wsk != nullptr && sl == 0) wsk[t * d.K + lane] = wl;
+  }
+}
+
+// One wave per (token, 1 KB slice); the slice is stored straight to `out`.
+// The duplicate-prologue path (and rows too wide to stage) use it.
+template <bool PROLOGUE, int KU>
+__global__ void __launch_bounds__(kThreads)
+    k_combine(Dims d, PlanArrays pa, const u32x4* __restrict__ y, const float* __restrict__ wnvs,
+              int weighted, const u32x4* __restrict__ fold, u32x4* __restrict__ out,
+              float* __restrict__ wsk) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int V = d.H / 8;
+  const int nsl = (V + kWave - 1) / kWave;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+  if (item >= (int64_t)d.R * d.S * nsl) return;
+  const int64_t t = item / nsl;
+  const int sl = (int)(item - t * nsl);
+  const int j = sl * kWave + lane;
+  // The dst entries are read before the plan's status is checked, so the two
+  // loads overlap; nothing read before the check is used unless it is zero.
+  int dl = 0;
+  if (lane < d.K) dl = pa.dst[t * d.K + lane];
+  if (pa.status[0] != 0) return;
+  int gl;
+  float wl;
+  combine_routes(d, wnvs, wsk, t, sl, lane, dl, gl, wl);
+  const u32x4 v = combine_slice<PROLOGUE, KU>(d, y, fold, weighted, lane, dl, gl, wl, j);
+  if (j < V) {
+    if (kCombineNtStore) __builtin_nontemporal_store(v, out + t * V + j);
+    else out[t * V + j] = v;
+  }
+}
+
+// Staged gather: a workgroup of 16 waves takes `tpb` consecutive tokens
+// (about 140 KB of output rows).  It first reads the tokens' dst entries and
+// route weights into LDS (and writes the weight gather w_sk, coalesced), so a
+// work item then waits only for its routed rows; it sums every slice into
+// LDS as k_combine does, then writes the tpb rows to `out` as one contiguous
+// run of non-temporal stores.
+template <int KU>
+__global__ void __launch_bounds__(kStageThreads)
+    k_combine_staged(Dims d, PlanArrays pa, const u32x4* __restrict__ y,
+                     const float* __restrict__ wnvs, int weighted, u32x4* __restrict__ out,
+                     float* __restrict__ wsk, int tpb) {
+  __shared__ u32x4 stage[kStageVec];
+  __shared__ int sg[kStageRoutes];
+  __shared__ float sw[kStageRoutes];
+  if (pa.status[0] != 0) return;  // the same word for every thread of the grid
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int V = d.H / 8;
+  const int nsl = (V + kWave - 1) / kWave;
+  const int64_t N = (int64_t)d.R * d.S;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int nt = (int)min((int64_t)tpb, N - t0);
+  const int nr = nt * d.K;  // routes of the workgroup's tokens, at most kStageRoutes
+  for (int i = threadIdx.x; i < nr; i += kStageThreads) {
+    const int g = (int)dst_global_row(pa.dst[t0 * d.K + i]);
+    const float w = wnvs != nullptr ? wnvs[g] : 0.0f;
+    sg[i] = g;
+    sw[i] = w;
+    if (wsk != nullptr) wsk[t0 * d.K + i] = w;
+  }
+  __syncthreads();
+  for (int it = wave; it < nt * nsl; it += kStageThreads / kWave) {
+    const int lt = it / nsl, sl = it - lt * nsl;
+    const int j = sl * kWave + lane;
+    int gl = 0;
+    float wl = 0.0f;
+    if (lane < d.K) {
+      gl = sg[lt * d.K + lane];
+      wl = sw[lt * d.K + lane];
+    }
+    const u32x4 v = combine_slice<false, KU>(d, y, nullptr, weighted, lane, 0, gl, wl, j);
+    if (j < V) stage[lt * V + j] = v;
+  }
+  __syncthreads();
+  const int n = nt * V;
+  u32x4* o = out + t0 * V;
+  for (int b = 0; b < n; b += kStageThreads * kStageBatch) {
+    u32x4 r[kStageBatch];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[q] = bf16_rne(acc[c][2 * q]) | (bf16_rne(acc[c][2 * q + 1]) << 16);
-      if (kCombineNtStore) __builtin_nontemporal_store(v, out + t * V + j);
-      else out[t * V + j] = v;
+    for (int u = 0; u < kStageBatch; ++u) {
+      const int i = b + u * kStageThreads + (int)threadIdx.x;
+      if (i < n) r[u] = stage[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kStageBatch; ++u) {
+      const int i = b + u * kStageThreads + (int)threadIdx.x;
+      if (i < n) __builtin_nontemporal_store(r[u], o + i);
     }
   }
 }
@@ -220,34 +309,62 @@ __global__ void k_prefetch_index(Dims d, PlanArrays pa, int32_t* __restrict__ ou
   out[i * 2 + 1] = e >= 0 ? e % d.Eg : -1;
 }
 
+// Tokens per staged workgroup: at most what its LDS holds; the count that
+// minimises rounds of workgroups (one per compute unit at a time) times the
+// time of one (its tokens plus a fixed part), so that the last round is not
+// left nearly empty and small calls still spread over the compute units.
+int stage_tokens(const Dims& d) {
+  const int hi = min(kStageVec / (d.H / 8), kStageRoutes / d.K);
+  const int64_t n = (int64_t)d.R * d.S;
+  const int64_t ncu = d.ncu > 0 ? d.ncu : 256;
+  int best = hi;
+  int64_t best_cost = -1;
+  for (int t = hi; t >= 1; --t) {
+    const int64_t rounds = ((n + t - 1) / t + ncu - 1) / ncu;
+    const int64_t cost = rounds * (t + kStageFixed);
+    if (best_cost < 0 || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y,
                           const float* wnvs, bool weighted, uint16_t* fold, uint16_t* out,
                           float* wsk, hipStream_t s) {
-  constexpr int SV = kCombineSliceVec, KU = kCombineUnroll;
-  const int nsl = (d.H / 8 + kWave * SV - 1) / (kWave * SV);
+  constexpr int KU = kCombineUnroll;
+  const int V = d.H / 8;
+  const int nsl = (V + kWave - 1) / kWave;
   const int64_t items = (int64_t)d.R * d.S * nsl;
   const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const auto* yv = reinterpret_cast<const u32x4*>(y);
   auto* fv = reinterpret_cast<u32x4*>(fold);
+  auto* ov = reinterpret_cast<u32x4*>(out);
   if (fold != nullptr && d.K > 1) {
     // persistent grid over (duplicate group, slice) items, sized like the gather
-    const int fnsl = (d.H / 8 + kWave - 1) / kWave;
-    const int64_t fw = (int64_t)d.R * d.S * fnsl;
-    const int64_t want = (fw + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t want = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     const int fblocks = (int)(want < kFoldBlocks ? (want > 0 ? want : 1) : kFoldBlocks);
     hipLaunchKernelGGL(k_combine_fold, dim3(fblocks), dim3(kThreads), 0, s, d, pa, yv, wnvs,
                        weighted ? 1 : 0, fv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_combine<true, SV, KU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, d,
-                       pa, yv, wnvs, weighted ? 1 : 0, fv, reinterpret_cast<u32x4*>(out), wsk);
+    hipLaunchKernelGGL((k_combine<true, KU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, d,
+                       pa, yv, wnvs, weighted ? 1 : 0, fv, ov, wsk);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_combine<false, SV, KU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, d,
-                     pa, yv, wnvs, weighted ? 1 : 0, nullptr, reinterpret_cast<u32x4*>(out), wsk);
+  if (V <= kStageVec) {
+    const int tpb = stage_tokens(d);
+    const int64_t n = (int64_t)d.R * d.S;
+    hipLaunchKernelGGL((k_combine_staged<kStageUnroll>), dim3((unsigned)((n + tpb - 1) / tpb)),
+                       dim3(kStageThreads), 0, s, d, pa, yv, wnvs, weighted ? 1 : 0, ov, wsk, tpb);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((k_combine<false, KU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, d, pa,
+                     yv, wnvs, weighted ? 1 : 0, nullptr, ov, wsk);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ struct Dims {
   int32_t rbits;           // bits needed for a rank id
   int32_t ctok;            // tokens per chunk (64 / K)
   int32_t tbits;           // bits needed for a token index inside a chunk
+  int32_t ncu;             // compute units of the device the shapes were set up on
 };
 
 // Planner scratch: owned by a context (one allocation), or the library's
