@@ -664,7 +664,7 @@ STALL_PASSES = [["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_RDREQ_su
                  "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "GRBM_GUI_ACTIVE"],
                 ["TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum", "TCC_TAG_STALL_sum",
                  "TCC_EA0_WRREQ_LEVEL_sum", "TCC_EA0_RDREQ_LEVEL_sum", "GRBM_GUI_ACTIVE"]]
-STALL_KERNELS = ["k_dispatch_scatter", "k_combine", "k_write_rows", "k_scatter_cached",
+STALL_KERNELS = ["k_dispatch_scatter", "k_combine_staged", "k_write_rows", "k_scatter_cached",
                  "k_read_rows", "k_fill", "k_read", "k_copy"]
 
 
@@ -814,7 +814,7 @@ def measure_step(moon, config, dev, stream, steps, warmup):
     # launch): algorithmic bytes per launch over the average launch duration
     # of back-to-back launches on the timed inputs.
     kernels = {}
-    for kname, call in (("k_dispatch_scatter", "dispatch"), ("k_combine", "combine")):
+    for kname, call in (("k_dispatch_scatter", "dispatch"), ("k_combine_staged", "combine")):
         nbytes = avg(call)
         ach = nbytes / (launch[call] * 1e-6) / 1e9
         kernels[kname] = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
@@ -980,8 +980,8 @@ def main():
         k = head["kernels"]
         k["k_dispatch_scatter"]["write_rows_us_over_launch_us"] = round(
             ceilings["write_rows"]["us"] / k["k_dispatch_scatter"]["avg_launch_us"], 4)
-        k["k_combine"]["read_rows_us_over_launch_us"] = round(
-            ceilings["read_rows"]["us"] / k["k_combine"]["avg_launch_us"], 4)
+        k["k_combine_staged"]["read_rows_us_over_launch_us"] = round(
+            ceilings["read_rows"]["us"] / k["k_combine_staged"]["avg_launch_us"], 4)
         # Sum of the parts, each at the rate the memory system gives it alone:
         # dispatch = its token-row reads at the contiguous read rate + the
         # rest (route rows, padding, weights) at the row-write rate; combine
@@ -991,7 +991,7 @@ def main():
         tok_bytes = 2 * head["H"] * head["R"] * head["S"]
         t_d = tok_bytes / rate["read"] + (nb0["dispatch"] - tok_bytes) / rate["write_rows"]
         t_c = tok_bytes / rate["fill"] + (nb0["combine"] - tok_bytes) / rate["read_rows"]
-        for kn, t in (("k_dispatch_scatter", t_d), ("k_combine", t_c)):
+        for kn, t in (("k_dispatch_scatter", t_d), ("k_combine_staged", t_c)):
             k[kn]["sum_of_parts_us"] = round(t, 2)
             k[kn]["sum_of_parts_over_launch_us"] = round(t / k[kn]["avg_launch_us"], 4)
         for kk in k.values():

@@ -32,7 +32,7 @@ def test_step_only_line(monkeypatch, capsys):
     assert d["value"] == pytest.approx((b["dispatch"] + b["combine"]) / (d["ms_per_step"] * 1e-3)
                                        / 1e9, rel=2e-3)
     # the roofline is the longer-running of the step's two bulk kernels
-    assert set(d["kernels"]) == {"k_dispatch_scatter", "k_combine"}
+    assert set(d["kernels"]) == {"k_dispatch_scatter", "k_combine_staged"}
     r = d["roofline"]
     assert r == max(d["kernels"].values(), key=lambda k: k["avg_launch_us"])
     for r in d["kernels"].values():
