@@ -12,7 +12,7 @@
 //                            and order as the one-pass dispatch scatter
 //   moon_ceiling_read_rows   combine's loads without its stores: for every
 //                            token, 1 KB slices of its K routed rows loaded
-//                            and discarded, the same grid as combine
+//                            and discarded, one wave per token slice
 //   moon_ceiling_scatter_cached  the one-pass dispatch scatter with its token
 //                            rows served from the cache: token t stores the
 //                            row of token t mod 4096 (58 MB at 14 KB rows,
