@@ -8,18 +8,20 @@
 //  destination rank into that rank's primary row in fp32.)
 //
 // k_combine_staged (the default): a workgroup of 16 waves owns a run of
-// consecutive tokens whose output rows fill about 140 KB of LDS.  A work item
-// is one wave on a slice of 64 vectors (512 bf16) of one token's row.  Lanes
-// 0..K-1 decode the token's K dst entries (both signs: every route owns its
-// row) and fetch the K route weights; the loop over k reads two routed slices
-// at a time with 16-byte loads, widens bf16 to fp32 and accumulates c_k * y
-// in ascending k with a separate multiply and add (the library is built with
-// -ffp-contract=off), then rounds once to bf16 (nearest, ties to even) into
-// LDS.  When all of its tokens are summed, the workgroup writes their rows as
-// one contiguous run.  Bound: HBM bandwidth (K row reads + one row write per
-// token); the long output runs write faster between the gathers than one
-// 1 KB store per slice does.  k_combine is the same sum stored slice by
-// slice, used by the duplicate-prologue path.
+// consecutive tokens whose output rows fill up to 140 KB of LDS.  It first
+// reads the run's dst entries (both signs: every route owns its row) and
+// route weights into LDS and writes the weight gather w_sk from there.  A work
+// item is one wave on a slice of 64 vectors (512 bf16) of one token's row: up
+// to eight routed slices are loaded at a time with 16-byte loads, widened to
+// fp32 and accumulated as c_k * y in ascending k with a separate multiply and
+// add (the library is built with -ffp-contract=off), then rounded once to
+// bf16 (nearest, ties to even) into LDS.  When all of its tokens are summed,
+// the workgroup writes their rows as one contiguous run.  Bound: HBM
+// bandwidth (K row reads + one row write per token); the long output runs
+// write faster between the gathers than one 1 KB store per slice does.
+// k_combine is the same sum, each wave fetching its token's dst entries and
+// weights itself and loading two routed slices at a time, stored slice by
+// slice; the duplicate-prologue path uses it.
 //
 // With the prologue, k_combine_fold first sums, per duplicate group and
 // slice, the primary row and its duplicate rows (ascending k, c_k * y in
