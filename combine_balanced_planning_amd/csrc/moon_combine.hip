@@ -49,11 +49,6 @@ constexpr int kStageVec = 140 * 1024 / 16;  // 16-byte vectors of staged output
 constexpr int kStageRoutes = 2048;          // routes whose dst and weight a workgroup stages
 constexpr int kStageBatch = 8;              // vectors a thread moves per write step
 constexpr int kStageUnroll = 8;             // routed rows loaded before they are summed
-// A staged workgroup's fixed cost beside its tokens, in tokens' worth of
-// time (fitted on MI355X: it makes 10 tokens of 14 KB rows per workgroup
-// beat 8 and 9 at 32768 and 131072 tokens, and 32 beat 35 at 16384 tokens of
-// 4 KB rows).
-constexpr int kStageFixed = 3;
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -242,17 +237,18 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// Staged gather: a workgroup of 16 waves takes `tpb` consecutive tokens
-// (about 140 KB of output rows).  It first reads the tokens' dst entries and
-// route weights into LDS (and writes the weight gather w_sk, coalesced), so a
-// work item then waits only for its routed rows; it sums every slice into
-// LDS as k_combine does, then writes the tpb rows to `out` as one contiguous
-// run of non-temporal stores.
+// Staged gather: a workgroup of 16 waves takes a run of consecutive tokens
+// (the first `nhi` workgroups lo + 1 tokens, the others lo; at most about
+// 140 KB of output rows).  It first reads the tokens' dst entries and route
+// weights into LDS (and writes the weight gather w_sk, coalesced), so a work
+// item then waits only for its routed rows; it sums every slice into LDS as
+// k_combine does, then writes the run's rows to `out` as one contiguous run
+// of non-temporal stores.
 template <int KU>
 __global__ void __launch_bounds__(kStageThreads)
     k_combine_staged(Dims d, PlanArrays pa, const u32x4* __restrict__ y,
                      const float* __restrict__ wnvs, int weighted, u32x4* __restrict__ out,
-                     float* __restrict__ wsk, int tpb) {
+                     float* __restrict__ wsk, int lo, int nhi) {
   __shared__ u32x4 stage[kStageVec];
   __shared__ int sg[kStageRoutes];
   __shared__ float sw[kStageRoutes];
@@ -260,9 +256,9 @@ __global__ void __launch_bounds__(kStageThreads)
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int V = d.H / 8;
   const int nsl = (V + kWave - 1) / kWave;
-  const int64_t N = (int64_t)d.R * d.S;
-  const int64_t t0 = (int64_t)blockIdx.x * tpb;
-  const int nt = (int)min((int64_t)tpb, N - t0);
+  const int64_t b = blockIdx.x;
+  const int64_t t0 = b < nhi ? b * (lo + 1) : (int64_t)nhi * (lo + 1) + (b - nhi) * lo;
+  const int nt = b < nhi ? lo + 1 : lo;
   const int nr = nt * d.K;  // routes of the workgroup's tokens, at most kStageRoutes
   for (int i = threadIdx.x; i < nr; i += kStageThreads) {
     const int g = (int)dst_global_row(pa.dst[t0 * d.K + i]);
@@ -311,25 +307,16 @@ __global__ void k_prefetch_index(Dims d, PlanArrays pa, int32_t* __restrict__ ou
   out[i * 2 + 1] = e >= 0 ? e % d.Eg : -1;
 }
 
-// Tokens per staged workgroup: at most what its LDS holds; the count that
-// minimises rounds of workgroups (one per compute unit at a time) times the
-// time of one (its tokens plus a fixed part), so that the last round is not
-// left nearly empty and small calls still spread over the compute units.
-int stage_tokens(const Dims& d) {
+// Staged workgroups: the fewest whole rounds of workgroups (one per compute
+// unit at a time) whose runs fit the LDS block, at most one workgroup per
+// token; the tokens are spread evenly over them (the first n % W get one
+// more), so every round is full and the runs stay as long as they can be.
+int64_t stage_groups(const Dims& d) {
   const int hi = min(kStageVec / (d.H / 8), kStageRoutes / d.K);
   const int64_t n = (int64_t)d.R * d.S;
   const int64_t ncu = d.ncu > 0 ? d.ncu : 256;
-  int best = hi;
-  int64_t best_cost = -1;
-  for (int t = hi; t >= 1; --t) {
-    const int64_t rounds = ((n + t - 1) / t + ncu - 1) / ncu;
-    const int64_t cost = rounds * (t + kStageFixed);
-    if (best_cost < 0 || cost < best_cost) {
-      best = t;
-      best_cost = cost;
-    }
-  }
-  return best;
+  const int64_t w = ((n + hi - 1) / hi + ncu - 1) / ncu * ncu;
+  return w < n ? w : n;
 }
 
 }  // namespace
@@ -359,10 +346,11 @@ hipError_t launch_combine(const Dims& d, const PlanArrays& pa, const uint16_t* y
     return hipGetLastError();
   }
   if (V <= kStageVec) {
-    const int tpb = stage_tokens(d);
     const int64_t n = (int64_t)d.R * d.S;
-    hipLaunchKernelGGL((k_combine_staged<kStageUnroll>), dim3((unsigned)((n + tpb - 1) / tpb)),
-                       dim3(kStageThreads), 0, s, d, pa, yv, wnvs, weighted ? 1 : 0, ov, wsk, tpb);
+    const int64_t w = stage_groups(d);
+    if (w > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_combine_staged<kStageUnroll>), dim3((unsigned)w), dim3(kStageThreads), 0,
+                       s, d, pa, yv, wnvs, weighted ? 1 : 0, ov, wsk, (int)(n / w), (int)(n % w));
     return hipGetLastError();
   }
   hipLaunchKernelGGL((k_combine<false, KU>), dim3((unsigned)blocks), dim3(kThreads), 0, s, d, pa,
