@@ -222,6 +222,69 @@ def test_fused_duplicates_and_unweighted_round_trip(env):
         moon.moon_ctx_destroy(ctx)
 
 
+# bf16 bit patterns of the special values (column j of every expert-output
+# row gets special value j): +Inf, -Inf, a NaN, -0, the smallest subnormals of
+# both signs, a mid subnormal, the largest finite value and its negative.
+SPECIAL_BF16 = np.array([0x7F80, 0xFF80, 0x7FC1, 0x8000, 0x0001, 0x8001, 0x0040, 0x7F7F,
+                         0xFF7F], np.uint16)
+
+
+@pytest.mark.parametrize("flags", ["weighted", "plain", "prologue"])
+def test_combine_special_values(env, flags):
+    """Expert outputs holding infinities, a NaN, -0, bf16 subnormals and the
+    largest finite values, with some tokens mixing +Inf and -Inf: the
+    combine's fp32 sum rounded to bf16 equals the oracle's bit for bit (any
+    NaN becomes 0x7FC0, overflow becomes an infinity, subnormal products are
+    kept, not flushed)."""
+    import torch
+    moon, dev = env
+    rng = np.random.default_rng(4242)
+    R, E, K, S, H, B, P = 2, 8, 4, 96, 64, 0, 4
+    topk = np.stack([rng.permutation(E)[:K] for _ in range(R * S)]).reshape(R, S, K).astype(
+        np.int32)
+    w = rng.random((R, S, K)).astype(np.float32)
+    w[:, ::5, 1] = 0.0  # zero weights meet infinities: 0 * Inf is NaN
+    ref = oracle.plan(topk, E, E // R, P)
+    hidden = synth.bf16_normal(1234, 0, R * S * H).reshape(R, S, H)
+    y = synth.bf16_normal(5678, 0, R * ref.NvS * H).reshape(R * ref.NvS, H).copy()
+    ns = SPECIAL_BF16.size
+    y[:, :ns] = SPECIAL_BF16
+    # columns ns..: every other row +Inf, the rest -Inf or subnormal, so a
+    # token's K rows mix them in route order
+    y[0::2, ns] = 0x7F80
+    y[1::2, ns] = 0xFF80
+    y[0::3, ns + 1] = 0x0003
+    y[1::3, ns + 1] = 0x8002
+    y[2::3, ns + 1] = 0x7F7F
+    say(f"[case] special values {flags}")
+    ctx = moon.moon_ctx_create(R, E, K, S, H, B, P)
+    plan = moon.moon_plan_create(ctx)
+    try:
+        moon.moon_plan(ctx, pt.to_dev(topk, dev), None, plan)
+        moon.moon_dispatch(ctx, plan, pt.bf16_to_dev(hidden, dev), pt.to_dev(w, dev))
+        _, wwin = moon.window_tensors(ctx)
+        _, ewwin = oracle.dispatch(ref, hidden, w)
+        out = torch.empty((R, S, H), dtype=torch.bfloat16, device=dev)
+        if flags == "prologue":
+            fl = moon.MOON_COMBINE_DUP_PROLOGUE | moon.MOON_COMBINE_WEIGHTED
+            eout = oracle.combine_prologue(ref, y, ewwin, weighted=True)[0]
+        else:
+            fl = moon.MOON_COMBINE_WEIGHTED if flags == "weighted" else 0
+            eout = oracle.combine(ref, y, ewwin, weighted=flags == "weighted", exact=False)[0]
+        moon.moon_combine(ctx, plan, pt.bf16_to_dev(y, dev), wwin, fl, out)
+        assert moon.moon_plan_status(plan) == moon.MOON_OK
+        got = pt.dev_bits(out)
+        bad = np.argwhere(got != eout)
+        assert bad.size == 0, (f"{len(bad)} outputs differ, first at {bad[0].tolist()}: "
+                               f"{got[tuple(bad[0])]:#06x} vs {eout[tuple(bad[0])]:#06x}")
+        # the special columns did produce special results
+        assert (got[..., 2] == 0x7FC0).all()  # a NaN in every routed row
+        assert ((got[..., ns] & 0x7FFF) >= 0x7F80).any()
+    finally:
+        moon.moon_plan_destroy(plan)
+        moon.moon_ctx_destroy(ctx)
+
+
 def test_clone_repeat_and_backward_reuse(env):
     """A plan is bit-reproducible, clone() copies it, and dispatching a second
     tensor with an existing plan (the backward path) needs no new planning."""
