@@ -450,7 +450,8 @@ int32_t orc_row_sources(int32_t R, int32_t E, int32_t K, int32_t S, int32_t B, i
 
 // Nearest bf16 of a double, ties to even, by exact scaling: bf16 keeps 8
 // significant bits for normal numbers and a fixed quantum of 2^-133 below
-// 2^-126.  Overflow past the largest finite bf16 gives infinity.
+// 2^-126.  Overflow past the largest finite bf16 gives infinity; any NaN gives
+// the quiet NaN 0x7FC0 (a reading: the pages say nothing of non-finite values).
 uint16_t orc_bf16_from_double(double v) {
   if (std::isnan(v)) return 0x7FC0;
   if (v == 0.0) return std::signbit(v) ? 0x8000 : 0x0000;

@@ -166,10 +166,24 @@ def test_bf16_rounding_against_torch_on_float32_values():
         rng.standard_normal(20000).astype(np.float32),
         (rng.standard_normal(2000) * 1e-39).astype(np.float32),  # subnormal range
         np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, 1.00390625, 1.01171875], np.float32),
+        # infinities, the largest finite float32 (rounds up to infinity) and
+        # the largest finite bf16, 0x7F7F (kept)
+        np.array([np.inf, -np.inf, 3.4028235e38, -3.4028235e38, 3.3895314e38, -3.3895314e38],
+                 np.float32),
     ])
     exp = _bits(x)
     got = np.array([oracle.bf16_from_double(float(v)) for v in x], np.uint16)
     assert (got == exp).all()
+
+
+def test_bf16_rounding_keeps_nan_a_nan():
+    """A NaN sum rounds to a bf16 NaN (exponent all ones, mantissa not zero),
+    whatever its sign or payload; which NaN is a convention (the oracle and
+    the kernels use 0x7FC0; torch's CPU conversion gives 0xFFFF)."""
+    for bits in (0x7FC00000, 0xFFC00000, 0x7F800001, 0x7FBFFFFF, 0xFFFFFFFF):
+        v = float(np.array([bits], np.uint32).view(np.float32)[0])
+        r = oracle.bf16_from_double(v)
+        assert (r & 0x7F80) == 0x7F80 and (r & 0x007F) != 0, (hex(bits), hex(r))
 
 
 def test_bf16_rounding_of_doubles_is_single_rounding():

@@ -71,6 +71,18 @@ MUTANTS = {
     "gathered_weight_of_first_route": ("    if (wsk != nullptr) wsk[k] = wk;",
                                        "    if (wsk != nullptr) wsk[k] = wat(decode_row(d[0]));"),
     "capacity_without_slot_padding": ("(Eg + B) * (int64_t)(P - 1)", "Eg * (int64_t)(P - 1)"),
+    "histogram_checks_rank_zero_only": ("for (int64_t j = 0; j < (int64_t)R * E; ++j)\n"
+                                        "      if ((int64_t)tpe[j] != cnt[j]) return ST_HISTOGRAM;",
+                                        "for (int64_t j = 0; j < (int64_t)E; ++j)\n"
+                                        "      if ((int64_t)tpe[j] != cnt[j]) return ST_HISTOGRAM;"),
+    "slot_budget_not_reported": ("if (over_budget) return ST_SLOT_BUDGET;",
+                                 "if (over_budget && false) return ST_SLOT_BUDGET;"),
+    "prefetch_index_owner_and_row_swapped": ("out[j * 2 + 0] = e >= 0 ? e / Eg : -1;\n"
+                                             "    out[j * 2 + 1] = e >= 0 ? e % Eg : -1;",
+                                             "out[j * 2 + 0] = e >= 0 ? e % Eg : -1;\n"
+                                             "    out[j * 2 + 1] = e >= 0 ? e / Eg : -1;"),
+    "nan_rounds_to_infinity": ("if (std::isnan(v)) return 0x7FC0;",
+                               "if (std::isnan(v)) return 0x7F80;"),
 }
 
 PIN_TESTS = ["tests/test_oracle_plan.py", "tests/test_oracle_data.py", "tests/test_oracle_weights.py"]
